@@ -1,0 +1,209 @@
+/*
+ * siglip.h -- C ABI of the MI355X (gfx950) SigLIP So400m/14 image encoder.
+ *
+ * The library runs the image-encoder forward pass described on the page
+ * "Single-layer SigLIP vision benchmark" (intro and mermaid figure): a
+ * 588->1152 patch-embedding GEMM with bias and learned positional
+ * embedding, pre-norm encoder layers (layernorm eps 1e-6, fused QKV
+ * projection, 16x72 multi-head self-attention, output projection and
+ * residual, GELU MLP 1152->4304->1152 and residual), a final layernorm and
+ * the MAP pooling head, returning [batch, 1, 1152].
+ *
+ * Conventions for every function below:
+ *   - extern "C", never throws, never aborts; returns a siglip_status.
+ *   - On failure, siglip_last_error() returns a thread-local message.
+ *   - "device" pointers are HIP device memory on the current device;
+ *     "host" pointers are ordinary CPU memory.
+ *   - hip_stream is a hipStream_t passed as void*; NULL means the null stream.
+ *   - Compute calls enqueue work on hip_stream and return without a host
+ *     synchronisation; results are valid once the stream has reached them.
+ */
+#ifndef SIGLIP_H_
+#define SIGLIP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SIGLIP_API __attribute__((visibility("default")))
+
+typedef enum {
+  SIGLIP_OK = 0,
+  SIGLIP_E_INVALID_ARG = -1,   /* null pointer, size out of range, bad option */
+  SIGLIP_E_BAD_BLOB = -2,      /* weight blob malformed, truncated or inconsistent */
+  SIGLIP_E_UNSUPPORTED = -3,   /* valid request this build cannot run (dims, device) */
+  SIGLIP_E_OUT_OF_MEMORY = -4, /* device allocation failed */
+  SIGLIP_E_HIP = -5            /* a HIP runtime call or kernel launch failed */
+} siglip_status;
+
+typedef struct siglip_model siglip_model; /* opaque; owned by the library */
+
+/* Options for siglip_create. */
+typedef struct {
+  /* Encoder layers to run: 0 = every layer in the blob, else 1..depth.
+   * The page's single-layer benchmark reduces depth 27 to one. */
+  int32_t layers;
+  /* Largest batch siglip_encode will accept; the workspace is sized for it. */
+  int32_t max_batch;
+  /* 0 = F16 GEMM operands; 1 = OCP e4m3 FP8 operands for every weight GEMM
+   * (page "Single-layer SigLIP vision benchmark", intro: "--fp8-scale=-4";
+   * both operands of a product share the scale, page "FP8 attention and
+   * resident image/embedding transfers", intro). Accumulation is F32 in
+   * both modes; attention products, layernorm, residuals and GELU stay
+   * F16 storage with F32 arithmetic. */
+  int32_t gemm_precision;
+  /* Power-of-two operand scale exponent for FP8 (the page uses -4): an
+   * operand x is stored as e4m3(x * 2^-exp), saturating at +-448, and each
+   * product is rescaled by 2^(2*exp). Ignored for F16. Range -8..8. */
+  int32_t fp8_scale_exp;
+} siglip_options;
+
+/*
+ * Parse a weight blob, upload and convert the weights once, allocate the
+ * workspace for opt->max_batch images. Parameters stay resident until
+ * siglip_destroy (page "SigLIP optimized execution and PV padding",
+ * "Full-model results": parameters uploaded once, inference calls repeat).
+ *
+ * blob:       host memory, blob_bytes long, read during the call only (the
+ *             caller may free it afterwards). Format, little-endian:
+ *             64-byte header {char magic[4]="SGLP"; u32 version=1; u32 width,
+ *             depth, heads, head_dim, mlp, tokens, patch_dim, dtype(0=F32);
+ *             u64 total_bytes; u8 reserved[16]}, then every parameter as
+ *             float32 at 64-byte aligned offsets in this order: embed.w
+ *             [patch_dim,width], embed.b [width], pos [tokens,width]; per
+ *             layer ln1.g, ln1.b [width], qkv.w [width,3*width], qkv.b,
+ *             out.w [width,width], out.b, ln2.g, ln2.b, mlp1.w [width,mlp],
+ *             mlp1.b [mlp], mlp2.w [mlp,width], mlp2.b; final_ln.g, .b;
+ *             map.probe [1,width], map.q.w [width,width], map.q.b,
+ *             map.kv.w [width,2*width], map.kv.b, map.out.w, map.out.b,
+ *             map.ln.g, map.ln.b, map.mlp1.w, map.mlp1.b, map.mlp2.w,
+ *             map.mlp2.b. Matrices are [in,out] row-major (y = x W).
+ * opt:        host pointer, read during the call.
+ * out:        receives the new model; set to NULL on failure.
+ * Errors: INVALID_ARG (null pointer, bad options), BAD_BLOB (checked on the
+ * CPU before any HIP call), UNSUPPORTED (dims this build cannot run: width
+ * != heads*head_dim, width % 128, head_dim > 80 or % 8, mlp % 8,
+ * patch_dim % 4, tokens > 4096, or a device that is not gfx950),
+ * OUT_OF_MEMORY, HIP. Blocks until the upload and conversion are complete.
+ */
+SIGLIP_API int siglip_create(const void* blob, size_t blob_bytes,
+                             const siglip_options* opt, siglip_model** out);
+
+/*
+ * Forward pass: patch-ordered F16 pixels to F16 embeddings.
+ *
+ * pixels_f16: device, [batch, tokens, patch_dim] F16 contiguous, in
+ *             [batch, patch_y, patch_x, y, x, channel] order (page
+ *             "Single-layer SigLIP vision benchmark", intro). Read only.
+ * batch:      1..max_batch.
+ * out_f16:    device, [batch, 1, width] F16 contiguous (page "Single-layer
+ *             SigLIP vision benchmark", intro: the probe axis is kept).
+ * hip_stream: stream to enqueue on.
+ * The model's workspace is shared by its calls: calls on one model must be
+ * ordered (one stream, or explicit synchronisation). Results are bitwise
+ * deterministic run to run. Errors: INVALID_ARG, HIP.
+ */
+SIGLIP_API int siglip_encode(siglip_model* m, const void* pixels_f16,
+                             int32_t batch, void* out_f16, void* hip_stream);
+
+/*
+ * Multi-head scaled dot-product attention alone, the encoder's attention
+ * step: for each image b and head h, o = softmax(q k^T * scale) v with F32
+ * softmax state (running maximum, denominator) and F32 accumulation; the
+ * result is rounded to F16 (page "Single-layer SigLIP vision benchmark",
+ * intro: attention explicitly converts its result back to F16; page
+ * "Capacity-first baseline", blocked attention keeps running max and
+ * denominator).
+ *
+ * q, k, v:     device F16; row r of image b starts at
+ *              ptr + (b*tokens + r)*row_stride_elems; head h occupies the
+ *              head_dim columns from h*head_dim. They may be three views
+ *              into one fused [.., 3*heads*head_dim] QKV buffer.
+ * o:           device F16 [batch, tokens, heads*head_dim] contiguous.
+ * Requires head_dim % 8 == 0, head_dim <= 80, row_stride_elems % 8 == 0
+ * and >= heads*head_dim, 16-byte aligned pointers, tokens >= 1. No data
+ * past token tokens-1 of an image or past column head_dim-1 of a head is
+ * read. Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+SIGLIP_API int siglip_attention(const void* q, const void* k, const void* v,
+                                int64_t row_stride_elems, void* o,
+                                int32_t batch, int32_t heads, int32_t tokens,
+                                int32_t head_dim, float scale, void* hip_stream);
+
+/* Free the model's device memory. Synchronises the device first. NULL is a
+ * no-op returning SIGLIP_OK. */
+SIGLIP_API int siglip_destroy(siglip_model* m);
+
+/* Static string naming a status code; never NULL. */
+SIGLIP_API const char* siglip_status_string(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+SIGLIP_API const char* siglip_last_error(void);
+
+/* Model dimensions as created: width, depth used, heads, head_dim, mlp,
+ * tokens, patch_dim, max_batch, gemm_precision (any pointer may be NULL). */
+SIGLIP_API int siglip_model_info(const siglip_model* m, int32_t* width,
+                                 int32_t* layers, int32_t* heads,
+                                 int32_t* head_dim, int32_t* mlp,
+                                 int32_t* tokens, int32_t* patch_dim,
+                                 int32_t* max_batch, int32_t* gemm_precision);
+
+/* ---------------------------------------------------------------------
+ * Diagnostics: per-stage checkpoints, the analogue of the operator
+ * checkpoints the pages validate against a host reference (page
+ * "Single-layer SigLIP vision benchmark", "Performance follow-up": 40
+ * operator checkpoints). Not needed for inference.
+ * ------------------------------------------------------------------- */
+typedef enum {
+  SIGLIP_STAGE_EMBED = 0,      /* [M, width]   F16  patch GEMM + bias + pos   */
+  SIGLIP_STAGE_LN1 = 1,        /* [M, width]   F16 | e4m3 code (FP8 mode)     */
+  SIGLIP_STAGE_QKV = 2,        /* [M, 3*width] F16                            */
+  SIGLIP_STAGE_ATTN = 3,       /* [M, width]   F16 | e4m3 code                */
+  SIGLIP_STAGE_H_ATTN = 4,     /* [M, width]   F16  after attention residual  */
+  SIGLIP_STAGE_LN2 = 5,        /* [M, width]   F16 | e4m3 code                */
+  SIGLIP_STAGE_MLP_HIDDEN = 6, /* [M, mlp_pad] F16 | e4m3 code (post-GELU)    */
+  SIGLIP_STAGE_H_OUT = 7,      /* [M, width]   F16  after MLP residual        */
+  SIGLIP_STAGE_FINAL_LN = 8,   /* [M, width]   F16 | e4m3 code                */
+  SIGLIP_STAGE_MAP_KV = 9,     /* [M, 2*width] F16                            */
+  SIGLIP_STAGE_MAP_ATTN = 10,  /* [B, width]   F16 | e4m3 code                */
+  SIGLIP_STAGE_MAP_Y = 11,     /* [B, width]   F16  MAP output projection     */
+  SIGLIP_STAGE_MAP_LN = 12,    /* [B, width]   F16 | e4m3 code                */
+  SIGLIP_STAGE_MAP_HIDDEN = 13,/* [B, mlp_pad] F16 | e4m3 code (post-GELU)    */
+  SIGLIP_STAGE_MAP_Q = 14,     /* [1, width]   F16  probe query (create time) */
+  SIGLIP_STAGE_COUNT = 15
+} siglip_stage;
+
+/* Capture stage outputs on later siglip_encode calls: layer-local stages
+ * (LN1..H_OUT) of encoder layer `layer` (0-based) and every other stage.
+ * layer < 0 turns capture off. Allocates the capture buffers (sized for
+ * max_batch) on first use. Errors: INVALID_ARG, OUT_OF_MEMORY. */
+SIGLIP_API int siglip_debug_capture(siglip_model* m, int32_t layer);
+
+/* Describe a captured stage of the last capturing encode: rows, columns
+ * holding data, row stride in elements and bytes per element (2 = F16,
+ * 1 = e4m3 code of x * 2^-fp8_scale_exp). Any pointer may be NULL. */
+SIGLIP_API int siglip_debug_stage_info(const siglip_model* m, int32_t stage,
+                                       int64_t* rows, int64_t* cols,
+                                       int64_t* ld, int32_t* elem_bytes);
+
+/* Copy a captured stage (rows*ld*elem_bytes bytes) to host memory dst of
+ * dst_bytes; synchronises the device. Errors: INVALID_ARG (capture off,
+ * stage out of range, dst too small), HIP. */
+SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage,
+                                  void* dst, size_t dst_bytes);
+
+/* Fill the whole workspace (every activation buffer, including row and
+ * column padding) with a 16-bit pattern, e.g. 0x7E00 (F16 NaN), to show
+ * that siglip_encode never reads data it did not write in the same call
+ * (page "Layout and barrier diagnosis", "Padding, SRAM placement and paired
+ * transfers": padding is read, so unwritten tails must not be). Synchronous. */
+SIGLIP_API int siglip_debug_fill_workspace(siglip_model* m, uint16_t pattern);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGLIP_H_ */

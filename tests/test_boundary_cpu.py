@@ -1,0 +1,145 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/siglip.h declares, and rejects malformed blobs, unsupported
+dimensions, bad options and null pointers with the documented status before
+any HIP call."""
+import ctypes
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import synthetic as S
+import vision_transformer_so400m_amd as V
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "siglip.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SIGLIP_API\s+[\w\s\*]+?\b(siglip_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(V.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = V.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert V.status_name(V.SIGLIP_OK) == "SIGLIP_OK"
+    assert V.status_name(V.SIGLIP_E_BAD_BLOB) == "SIGLIP_E_BAD_BLOB"
+    assert V.status_name(12345) == "SIGLIP_E_UNKNOWN"
+
+
+@pytest.fixture(scope="module")
+def blob1():
+    d = S.SO400M.with_depth(1)
+    return bytes(S.pack_blob(d, S.make_weights(d, 0)))
+
+
+def _create(blob, **kw):
+    with pytest.raises(V.SiglipError) as ei:
+        V.Model(blob, **kw)
+    return ei.value
+
+
+def _patched(blob, off, fmt, value):
+    b = bytearray(blob)
+    struct.pack_into(fmt, b, off, value)
+    return bytes(b)
+
+
+@pytest.mark.parametrize("case,mutate,status,msg", [
+    ("magic", lambda b: b"XXXX" + b[4:], V.SIGLIP_E_BAD_BLOB, "magic"),
+    ("version", lambda b: _patched(b, 4, "<I", 2), V.SIGLIP_E_BAD_BLOB, "version"),
+    ("dtype", lambda b: _patched(b, 36, "<I", 1), V.SIGLIP_E_BAD_BLOB, "dtype"),
+    ("zero_dim", lambda b: _patched(b, 28, "<I", 0), V.SIGLIP_E_BAD_BLOB, "zero"),
+    ("heads_x_dim", lambda b: _patched(b, 16, "<I", 15), V.SIGLIP_E_BAD_BLOB, "heads"),
+    ("truncated", lambda b: b[:-64], V.SIGLIP_E_BAD_BLOB, "size"),
+    ("total_mismatch", lambda b: _patched(b, 40, "<Q", len(b) + 64) , V.SIGLIP_E_BAD_BLOB, "total_bytes"),
+    ("short", lambda b: b[:32], V.SIGLIP_E_BAD_BLOB, "header"),
+])
+def test_bad_blobs_are_rejected_on_cpu(blob1, case, mutate, status, msg):
+    e = _create(mutate(blob1))
+    assert e.status == status, e
+    assert msg in e.message
+
+
+def test_truncated_with_consistent_header(blob1):
+    # header claims the shorter size: the tensor walk must find the truncation
+    b = bytearray(blob1[:-4096])
+    struct.pack_into("<Q", b, 40, len(b))
+    e = _create(bytes(b))
+    assert e.status == V.SIGLIP_E_BAD_BLOB and "truncated" in e.message
+
+
+def test_depth_mismatch_is_truncation(blob1):
+    b = _patched(blob1, 12, "<I", 2)   # claims 2 layers, holds 1
+    e = _create(b)
+    assert e.status == V.SIGLIP_E_BAD_BLOB
+
+
+def test_trailing_bytes(blob1):
+    b = bytearray(blob1) + bytes(64)
+    struct.pack_into("<Q", b, 40, len(b))
+    e = _create(bytes(b))
+    assert e.status == V.SIGLIP_E_BAD_BLOB and "trailing" in e.message
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(max_batch=0), "max_batch"),
+    (dict(max_batch=5000), "max_batch"),
+    (dict(layers=2), "layers"),
+    (dict(layers=-1), "layers"),
+    (dict(fp8=True, fp8_scale_exp=9), "fp8_scale_exp"),
+])
+def test_bad_options(blob1, kw, msg):
+    e = _create(blob1, **kw)
+    assert e.status == V.SIGLIP_E_INVALID_ARG and msg in e.message
+
+
+def test_unsupported_width_is_reported_before_the_device():
+    d = S.small_dims(1)   # width 144: not a multiple of 128
+    e = _create(bytes(S.pack_blob(d, S.make_weights(d, 0))))
+    assert e.status == V.SIGLIP_E_UNSUPPORTED and "128" in e.message
+
+
+def test_null_pointers_and_bad_attention_args():
+    lib = V.load_library()
+    out = ctypes.c_void_p()
+    opt = V.siglip_options(0, 1, 0, -4)
+    assert lib.siglip_create(None, 0, ctypes.byref(opt), ctypes.byref(out)) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_create(b"x" * 64, 64, None, ctypes.byref(out)) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_create(b"x" * 64, 64, ctypes.byref(opt), None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_encode(None, None, 1, None, None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_destroy(None) == V.SIGLIP_OK
+    assert lib.siglip_debug_capture(None, 0) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_debug_fill_workspace(None, 0) == V.SIGLIP_E_INVALID_ARG
+    # attention argument checks: every call below fails validation, so no
+    # kernel is ever launched on the bogus pointer
+    p = 4096
+    assert lib.siglip_attention(None, p, p, 1152, p, 1, 16, 729, 72, 0.1, None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_attention(p, p, p, 2048, p, 1, 16, 729, 128, 0.1, None) == V.SIGLIP_E_UNSUPPORTED
+    assert lib.siglip_attention(p, p, p, 1152, p, 1, 16, 729, 76, 0.1, None) == V.SIGLIP_E_UNSUPPORTED
+    assert lib.siglip_attention(p, p, p, 1000, p, 1, 16, 729, 72, 0.1, None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_attention(p, p, p, 1152, p, 0, 16, 729, 72, 0.1, None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_attention(p + 8, p, p, 1152, p, 1, 16, 729, 72, 0.1, None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_attention(p, p, p, 1152, p, 1, 16, 729, 72, -1.0, None) == V.SIGLIP_E_INVALID_ARG
+    assert "scale" in V.last_error()
+
+
+def test_e4m3_decode_helper_matches_oracle_rounding():
+    import oracle as O
+    codes = np.arange(256, dtype=np.uint8)
+    vals = V.e4m3_decode(codes, scale_exp=0)
+    finite = ~np.isnan(vals)
+    assert finite.sum() == 254
+    np.testing.assert_array_equal(O.e4m3_round(vals[finite]), vals[finite])

@@ -1,0 +1,433 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Two kinds of comparison, both on the same seeded inputs:
+
+* Stage by stage (per kernel): each captured stage is compared with the
+  oracle function applied to the GPU's own previous-stage output, with the
+  weights at the device's operand precision (F16, or e4m3 at scale 2^-4).
+  What remains is the kernel's own rounding, so the bound is tight:
+  |gpu - ref| <= ulp_f16(ref) + 8 sqrt(K) 2^-24 (|x| @ |w|), i.e. one F16
+  unit in the last place for the output rounding plus an 8-sigma random-walk
+  bound on F32 accumulation-order differences over K terms. Attention adds
+  the F16 rounding of the probabilities before the PV product:
+  2^-11 max|v| per head. e4m3 outputs must be the nearest code of 2^4 ref,
+  or its other neighbour where 2^4 ref lies within the GPU-side error of
+  the pre-quantization value (plus 1e-4 relative) of a rounding midpoint:
+  there both sides round the same quantity computed in different precisions.
+
+* End to end: the encoder output against the plain float64 oracle with the
+  stated bars: one layer, F16: per image cosine >= 0.999 and max abs error
+  <= 2e-2; 27 layers (F16 or FP8 operands): cosine >= 0.99, max abs <= 0.5.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synthetic as S
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def V():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import vision_transformer_so400m_amd as lib
+    lib.load_library()
+    return lib
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ helpers
+
+def ulp16(v):
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def acc_tol(x, w):
+    """8-sigma random-walk bound of F32 accumulation differences over K."""
+    k = x.shape[-1]
+    return 8.0 * math.sqrt(k) * 2.0 ** -24 * (np.abs(x) @ np.abs(w))
+
+
+def assert_close(name, gpu, ref, extra=0.0, ulps=1.0):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), f"{name}: non-finite values"
+    err = np.abs(gpu - ref)
+    tol = ulps * ulp16(ref) + extra
+    bad = err > tol
+    _flush(f"  {name}: max err {err.max():.3e}, max err/tol {np.max(err / tol):.3f}")
+    assert not bad.any(), (f"{name}: {bad.sum()} of {bad.size} beyond tolerance; worst at "
+                           f"{np.unravel_index(np.argmax(err / tol), err.shape)}")
+
+
+_E4M3_POS = None
+
+
+def e4m3_neighbours_ok(name, codes, ref, scale_exp, band=0.0):
+    """GPU e4m3 codes against exact values ref (in activation units).
+
+    The code must be the nearest e4m3 value of ref * 2^-scale_exp, except
+    where that value lies within `band` (the GPU-side error of the value
+    before quantization, plus 1e-4 relative) of a rounding midpoint: there
+    either neighbour is accepted."""
+    global _E4M3_POS
+    import vision_transformer_so400m_amd as Vm
+    if _E4M3_POS is None:
+        v = Vm.e4m3_decode(np.arange(256, dtype=np.uint8), 0)
+        _E4M3_POS = np.unique(np.abs(v[np.isfinite(v)]))
+    got = Vm.e4m3_decode(codes, 0)
+    assert np.isfinite(got).all(), f"{name}: NaN codes"
+    s = 2.0 ** -scale_exp
+    r = np.clip(np.asarray(ref, np.float64) * s, -448, 448)
+    a = np.abs(r)
+    i = np.searchsorted(_E4M3_POS, a)
+    upper = _E4M3_POS[np.minimum(i, len(_E4M3_POS) - 1)]
+    lower = np.where(_E4M3_POS[np.minimum(i, len(_E4M3_POS) - 1)] == a, a, _E4M3_POS[np.maximum(i - 1, 0)])
+    near = np.sign(r) * O.e4m3_round(a)
+    mid = 0.5 * (lower + upper)
+    ambiguous = np.abs(a - mid) <= np.asarray(band) * s + 1e-4 * a + 1e-9
+    other = np.sign(r) * np.where(np.abs(near) == upper, lower, upper)
+    ok = (got == near) | (ambiguous & (got == other)) | ((got == 0) & (near == 0))
+    _flush(f"  {name}: {int((~ok).sum())} bad codes, {int((got != near).sum())} off-nearest, "
+           f"{int(ambiguous.sum())} near a midpoint")
+    assert ok.all(), f"{name}: worst at {np.argwhere(~ok)[:5].tolist()}"
+
+
+def device_weight(wt, name, fp8, scale_exp=-4):
+    w = np.asarray(wt[name], np.float64)
+    if fp8:
+        return O.fp8_operand(w, scale_exp)
+    return w.astype(np.float16).astype(np.float64)
+
+
+def make_model(V, dims, seed, max_batch, fp8=False, layers=0):
+    wt = S.make_weights(dims, seed)
+    blob = S.pack_blob(dims, wt)
+    return V.Model(blob, layers=layers, max_batch=max_batch, fp8=fp8), wt
+
+
+def run(model, x_np):
+    x = torch.from_numpy(x_np).cuda()
+    y = model.encode(x)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def per_image_metrics(gpu, ref):
+    g = np.asarray(gpu, np.float64).reshape(gpu.shape[0], -1)
+    r = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    cos = (g * r).sum(1) / np.linalg.norm(g, axis=1) / np.linalg.norm(r, axis=1)
+    return cos, np.abs(g - r).max(1)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_ref(q, k, v, heads, d, scale):
+    """Oracle attention per image and head: q,k,v [B,T,heads*d] -> [B,T,heads*d]."""
+    qh, kh, vh = (O.split_heads(a.astype(np.float64), heads) for a in (q, k, v))
+    return O.merge_heads(O.attention(qh, kh, vh, scale))
+
+
+def _attn_extra(v, heads, d):
+    # probability rounding to F16 before PV: 2^-11 * max|v| of the head
+    vh = np.abs(O.split_heads(v.astype(np.float64), heads)).max(axis=(-1, -2), keepdims=True)
+    return O.merge_heads(np.broadcast_to(vh, vh.shape[:-2] + (v.shape[1], d))) * 2.0 ** -11
+
+
+@pytest.mark.parametrize("t", [1, 4, 63, 64, 65, 127, 128, 129, 300])
+@pytest.mark.parametrize("d", [72, 64, 80, 8])
+def test_attention_shapes(V, t, d):
+    heads, b = 2, 2
+    _flush(f"attention t={t} d={d}")
+    rng = np.random.default_rng(100 + t + d)
+    q, k, v = (rng.standard_normal((b, t, heads * d), dtype=np.float32).astype(np.float16) for _ in range(3))
+    scale = 1 / math.sqrt(d)
+    out = V.attention(*(torch.from_numpy(a).cuda() for a in (q, k, v)), heads, d, scale)
+    torch.cuda.synchronize()
+    ref = _attn_ref(q, k, v, heads, d, scale)
+    assert_close(f"attn t{t} d{d}", out.cpu().numpy(), ref, extra=_attn_extra(v, heads, d) + 1e-6)
+
+
+def test_attention_fused_views_never_read_padding(V):
+    """Q/K/V as views into a fused row with gap columns; rows after the last
+    image and the gap columns hold NaN. Output must equal the clean run
+    bit for bit."""
+    b, t, heads, d = 3, 729, 16, 72
+    w = heads * d
+    ld = 3 * w + 8
+    rng = np.random.default_rng(7)
+    qkv = rng.standard_normal((b * t, 3 * w), dtype=np.float32).astype(np.float16)
+    res = []
+    for poison in (False, True):
+        buf = np.full((b * t + 64, ld), np.nan if poison else 0.0, np.float16)
+        buf[: b * t, : 3 * w] = qkv
+        g = torch.from_numpy(buf).cuda()
+        base = g.reshape(-1)
+        q, k, v = base[0:], base[w:], base[2 * w:]
+        out = V.attention(q, k, v, heads, d, 1 / math.sqrt(d), row_stride=ld, tokens=t, batch=b,
+                          out=torch.empty((b, t, w), dtype=torch.float16, device="cuda"))
+        torch.cuda.synchronize()
+        res.append(out.cpu().numpy())
+    assert np.isfinite(res[1]).all()
+    np.testing.assert_array_equal(res[0].view(np.uint16), res[1].view(np.uint16))
+    ref = _attn_ref(qkv[:, :w].reshape(b, t, w), qkv[:, w:2 * w].reshape(b, t, w),
+                    qkv[:, 2 * w:].reshape(b, t, w), heads, d, 1 / math.sqrt(d))
+    assert_close("fused views", res[0], ref, extra=_attn_extra(qkv[:, 2 * w:].reshape(b, t, w), heads, d) + 1e-6)
+
+
+def test_attention_c2_full_size_sampled(V):
+    """The attention workload at full size: [32, 729, 16 x 72], seeds (0,2),
+    (0,3), (0,4), checked on 24 sampled (image, head) pairs."""
+    cfg = S.CONFIGS["c2_attention_b32"]
+    q, k, v = S.make_attention_inputs(cfg["batch"], cfg["tokens"], cfg["heads"], cfg["head_dim"], cfg["seeds"])
+    heads, d = cfg["heads"], cfg["head_dim"]
+    _flush("attention c2 full size")
+    out = V.attention(*(torch.from_numpy(a).cuda() for a in (q, k, v)), heads, d, 1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all()
+    rng = np.random.default_rng(0)
+    for bi, hi in zip(rng.integers(0, 32, 24), rng.integers(0, 16, 24)):
+        sl = slice(hi * d, (hi + 1) * d)
+        ref = O.attention(q[bi, :, sl].astype(np.float64), k[bi, :, sl].astype(np.float64),
+                          v[bi, :, sl].astype(np.float64), 1 / math.sqrt(d))
+        extra = np.abs(v[bi, :, sl].astype(np.float64)).max() * 2.0 ** -11 + 1e-6
+        assert_close(f"c2 b{bi} h{hi}", o[bi, :, sl], ref, extra=extra)
+
+
+# ------------------------------------------------------------------ encoder
+
+def _stage(model, name):
+    return model.debug_stage(name)
+
+
+def _dec(model, arr, fp8):
+    import vision_transformer_so400m_amd as Vm
+    if fp8 and arr.dtype == np.uint8:
+        return Vm.e4m3_decode(arr, model.fp8_scale_exp)
+    return arr.astype(np.float64)
+
+
+def check_stages(model, wt, x, dims, fp8, batch):
+    """Every captured stage of layer 0 against the oracle on the GPU's inputs."""
+    se = model.fp8_scale_exp
+    M, W, T, F, H, D = batch * dims.tokens, dims.width, dims.tokens, dims.mlp, dims.heads, dims.head_dim
+    st = {n: _stage(model, n) for n in
+          ["EMBED", "LN1", "QKV", "ATTN", "H_ATTN", "LN2", "MLP_HIDDEN", "H_OUT", "FINAL_LN",
+           "MAP_KV", "MAP_ATTN", "MAP_Y", "MAP_LN", "MAP_HIDDEN", "MAP_Q"]}
+    dw = lambda n: device_weight(wt, n, fp8, se)
+    f = lambda n: _dec(model, st[n], fp8)
+
+    def gemm_check(name, xin, wname, bname, add=None, gelu=False):
+        w = dw(wname)
+        ref = O.linear(xin, w, wt[bname].astype(np.float64))
+        extra = acc_tol(xin, w)
+        if add is not None:
+            ref = ref + add
+        if gelu:
+            ref = O.gelu_tanh(ref)
+            extra = extra * 1.2
+        if fp8 and st[name].dtype == np.uint8:
+            e4m3_neighbours_ok(name, st[name], ref, se, band=extra)
+        else:
+            assert_close(name, st[name], ref, extra=extra + 1e-6)
+
+    def ln_check(name, hin, p):
+        ref = O.layer_norm(hin, wt[p + ".g"].astype(np.float64), wt[p + ".b"].astype(np.float64))
+        if fp8:
+            e4m3_neighbours_ok(name, st[name], ref, se, band=1e-5)
+        else:
+            assert_close(name, st[name], ref, extra=1e-5)
+
+    xin = x.reshape(M, dims.patch_dim).astype(np.float64)
+    if fp8:
+        xin = O.fp8_operand(xin, se)
+    pos = np.tile(wt["pos"].astype(np.float64), (batch, 1))
+    gemm_check("EMBED", xin, "embed.w", "embed.b", add=pos)
+    ln_check("LN1", f("EMBED"), "layer0.ln1")
+    gemm_check("QKV", f("LN1"), "layer0.qkv.w", "layer0.qkv.b")
+    qkv = f("QKV").reshape(batch, T, 3 * W)
+    ref_attn = _attn_ref(qkv[..., :W], qkv[..., W:2 * W], qkv[..., 2 * W:], H, D, 1 / math.sqrt(D)).reshape(M, W)
+    attn_extra = _attn_extra(qkv[..., 2 * W:], H, D).reshape(M, W) + 1e-6
+    if fp8:
+        e4m3_neighbours_ok("ATTN", st["ATTN"], ref_attn, se, band=attn_extra)
+    else:
+        assert_close("ATTN", st["ATTN"], ref_attn, extra=attn_extra)
+    gemm_check("H_ATTN", f("ATTN"), "layer0.out.w", "layer0.out.b", add=f("EMBED"))
+    ln_check("LN2", f("H_ATTN"), "layer0.ln2")
+    gemm_check("MLP_HIDDEN", f("LN2"), "layer0.mlp1.w", "layer0.mlp1.b", gelu=True)
+    pad = model.debug_stage("MLP_HIDDEN", full=True)[:, F:]
+    assert pad.size and not pad.view(np.uint8).any(), "MLP padding columns must be exact zeros"
+    gemm_check("H_OUT", f("MLP_HIDDEN"), "layer0.mlp2.w", "layer0.mlp2.b", add=f("H_ATTN"))
+    if model.layers == 1:
+        ln_check("FINAL_LN", f("H_OUT"), "final_ln")
+    # the probe is an operand of the device GEMM: F16 or e4m3, like every activation
+    probe = device_weight(wt, "map.probe", fp8, se)
+    gemm_check("MAP_Q", probe, "map.q.w", "map.q.b")
+    gemm_check("MAP_KV", f("FINAL_LN"), "map.kv.w", "map.kv.b")
+    kv = f("MAP_KV").reshape(batch, T, 2 * W)
+    qm = np.broadcast_to(f("MAP_Q").reshape(1, 1, W), (batch, 1, W))
+    ref_m = _attn_ref(qm, kv[..., :W], kv[..., W:], H, D, 1 / math.sqrt(D)).reshape(batch, W)
+    if fp8:
+        e4m3_neighbours_ok("MAP_ATTN", st["MAP_ATTN"], ref_m, se, band=1e-5)
+    else:
+        assert_close("MAP_ATTN", st["MAP_ATTN"], ref_m, extra=1e-5)
+    gemm_check("MAP_Y", f("MAP_ATTN"), "map.out.w", "map.out.b")
+    ln_check("MAP_LN", f("MAP_Y"), "map.ln")
+    gemm_check("MAP_HIDDEN", f("MAP_LN"), "map.mlp1.w", "map.mlp1.b", gelu=True)
+    return st
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
+def test_c0_single_layer_stage_by_stage_and_end_to_end(V, fp8):
+    cfg = S.CONFIGS["c0_1layer_b1_f16"]
+    dims = S.SO400M.with_depth(1)
+    _flush(f"c0 stages fp8={fp8}")
+    model, wt = make_model(V, dims, cfg["seed"], max_batch=1, fp8=fp8)
+    model.debug_capture(0)
+    x = S.make_pixels(dims, 1, cfg["seed"])
+    y = run(model, x)
+    check_stages(model, wt, x, dims, fp8, 1)
+    # last step: out = MAP_Y + MLP(...) written straight to the caller's buffer
+    f = lambda n: _dec(model, model.debug_stage(n), fp8)
+    w2 = device_weight(wt, "map.mlp2.w", fp8)
+    ref = O.linear(f("MAP_HIDDEN"), w2, wt["map.mlp2.b"].astype(np.float64)) + f("MAP_Y")
+    assert_close("OUT", y.reshape(1, -1), ref, extra=acc_tol(f("MAP_HIDDEN"), w2) + 1e-6)
+    info = model.debug_stage_info("MLP_HIDDEN")
+    assert info[1] == 4304 and info[2] == 4352
+    # end to end against the plain oracle
+    ref = O.encode(wt, x, dims.heads)
+    cos, mx = per_image_metrics(y, ref)
+    _flush(f"  c0 end-to-end fp8={fp8}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    if not fp8:
+        assert cos.min() >= 0.999 and mx.max() <= 2e-2
+    else:
+        assert cos.min() >= 0.99 and mx.max() <= 0.5
+
+
+def test_c1_batch8_and_prefix_bitwise(V):
+    cfg = S.CONFIGS["c1_1layer_b8_f16"]
+    dims = S.SO400M.with_depth(1)
+    _flush("c1 batch 8")
+    model, wt = make_model(V, dims, cfg["seed"], max_batch=8)
+    model.debug_capture(0)
+    x = S.make_pixels(dims, 8, cfg["seed"])
+    y = run(model, x)
+    check_stages(model, wt, x, dims, False, 8)
+    ref = O.encode(wt, x, dims.heads)
+    cos, mx = per_image_metrics(y, ref)
+    _flush(f"  c1 end-to-end: min cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    assert cos.min() >= 0.999 and mx.max() <= 2e-2
+    # image 0 of the batch equals the single-image run (different tile shapes,
+    # same accumulation order)
+    m1, _ = make_model(V, dims, cfg["seed"], max_batch=1)
+    y1 = run(m1, x[:1])
+    np.testing.assert_array_equal(y[:1].view(np.uint16), y1.view(np.uint16))
+
+
+def test_determinism_and_nan_poisoned_workspace(V):
+    dims = S.SO400M.with_depth(1)
+    _flush("determinism + NaN poison")
+    model, wt = make_model(V, dims, 0, max_batch=3)
+    x = S.make_pixels(dims, 3, 4)
+    xt = torch.from_numpy(x).cuda()
+    model.debug_fill_workspace(0)
+    ref = model.encode(xt).cpu().numpy()
+    outs = [model.encode(xt) for _ in range(20)]
+    torch.cuda.synchronize()
+    for o in outs:
+        np.testing.assert_array_equal(o.cpu().numpy().view(np.uint16), ref.view(np.uint16))
+    model.debug_fill_workspace(0x7E00)   # F16 NaN everywhere, padding included
+    y = model.encode(xt[:2]).cpu().numpy()
+    np.testing.assert_array_equal(y.view(np.uint16), ref[:2].view(np.uint16))
+    # FP8 path too
+    model8, _ = make_model(V, dims, 0, max_batch=3, fp8=True)
+    model8.debug_fill_workspace(0)
+    a = model8.encode(xt).cpu().numpy()
+    model8.debug_fill_workspace(0x7E00)
+    b = model8.encode(xt).cpu().numpy()
+    np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.isfinite(a).all()
+
+
+def test_four_token_full_width_diagnostic(V):
+    dims = S.four_token_dims(2)
+    _flush("four-token diagnostic")
+    model, wt = make_model(V, dims, 11, max_batch=3)
+    x = S.make_pixels(dims, 3, 11)
+    y = run(model, x)
+    ref = O.encode(wt, x, dims.heads)
+    cos, mx = per_image_metrics(y, ref)
+    _flush(f"  four-token: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    assert cos.min() >= 0.999 and mx.max() <= 2e-2
+
+
+def test_encode_argument_errors(V):
+    dims = S.SO400M.with_depth(1)
+    model, _ = make_model(V, dims, 0, max_batch=2)
+    x = torch.zeros((3, 729, 588), dtype=torch.float16, device="cuda")
+    out = torch.empty((3, 1, 1152), dtype=torch.float16, device="cuda")
+    lib = V.load_library()
+    st = lib.siglip_encode(model.handle, x.data_ptr(), 3, out.data_ptr(), None)
+    assert st == V.SIGLIP_E_INVALID_ARG and "max_batch" in V.last_error()
+    assert lib.siglip_encode(model.handle, x.data_ptr(), 0, out.data_ptr(), None) == V.SIGLIP_E_INVALID_ARG
+    assert lib.siglip_debug_capture(model.handle, 5) == V.SIGLIP_E_INVALID_ARG
+
+
+def _golden(name):
+    return np.load(os.path.join(HERE, "golden", name), allow_pickle=False)
+
+
+def _checksums(wt, x):
+    return np.array([float(np.sum(x, dtype=np.float64)), float(np.sum(wt["embed.w"], dtype=np.float64)),
+                     float(np.sum(wt["layer26.mlp2.w"], dtype=np.float64)),
+                     float(np.sum(wt["map.mlp2.w"], dtype=np.float64))])
+
+
+def test_c3_27_layers_f16_b1_b2(V):
+    g = _golden("oracle_c3_27layer_seed1.npz")
+    dims = S.SO400M
+    _flush("c3 27 layers F16")
+    wt = S.make_weights(dims, 1)
+    x = S.make_pixels(dims, 2, 1)
+    np.testing.assert_allclose(_checksums(wt, x), g["checksums"], rtol=1e-12)
+    model = V.Model(S.pack_blob(dims, wt), max_batch=2)
+    del wt
+    for b in (1, 2):
+        y = run(model, x[:b])
+        cos, mx = per_image_metrics(y, g["out"][:b, None, :])
+        _flush(f"  c3 B={b}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+        assert cos.min() >= 0.99 and mx.max() <= 0.5
+
+
+def test_c4_27_layers_fp8_b64_sampled(V):
+    g = _golden("oracle_c4_27layer_seed2.npz")
+    dims = S.SO400M
+    _flush("c4 27 layers FP8 B=64")
+    wt = S.make_weights(dims, 2)
+    x = S.make_pixels(dims, 64, 2)
+    np.testing.assert_allclose(_checksums(wt, x), g["checksums"], rtol=1e-12)
+    model = V.Model(S.pack_blob(dims, wt), max_batch=64, fp8=True)
+    del wt
+    y = run(model, x)
+    assert np.isfinite(y).all()
+    idx = g["images"]
+    cos, mx = per_image_metrics(y[idx], g["out"][:, None, :])
+    cq, mq = per_image_metrics(y[idx], g["out_fp8_operands"][:, None, :])
+    _flush(f"  c4 vs unquantized oracle: cosine {cos.min():.6f}, max abs {mx.max():.4e}; "
+           f"vs e4m3-operand oracle: cosine {cq.min():.6f}, max abs {mq.max():.4e}")
+    assert cos.min() >= 0.99 and mx.max() <= 0.5

@@ -1,0 +1,220 @@
+"""ctypes binding of libsiglip (include/siglip.h), same names as the C ABI.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of libsiglip.so. PyTorch supplies device memory and the stream.
+There is no CPU fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsiglip.so")
+
+SIGLIP_OK = 0
+SIGLIP_E_INVALID_ARG = -1
+SIGLIP_E_BAD_BLOB = -2
+SIGLIP_E_UNSUPPORTED = -3
+SIGLIP_E_OUT_OF_MEMORY = -4
+SIGLIP_E_HIP = -5
+
+STAGES = ["EMBED", "LN1", "QKV", "ATTN", "H_ATTN", "LN2", "MLP_HIDDEN", "H_OUT",
+          "FINAL_LN", "MAP_KV", "MAP_ATTN", "MAP_Y", "MAP_LN", "MAP_HIDDEN", "MAP_Q"]
+STAGE = {n: i for i, n in enumerate(STAGES)}
+
+EXPORTED = ["siglip_create", "siglip_encode", "siglip_attention", "siglip_destroy",
+            "siglip_status_string", "siglip_last_error", "siglip_model_info",
+            "siglip_debug_capture", "siglip_debug_stage_info", "siglip_debug_stage",
+            "siglip_debug_fill_workspace"]
+
+
+class SiglipError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class siglip_options(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("gemm_precision", ctypes.c_int32), ("fp8_scale_exp", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsiglip.so (built in-tree by build.build()); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m vision_transformer_so400m_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P = ctypes.POINTER
+    lib.siglip_create.argtypes = [vp, ctypes.c_size_t, P(siglip_options), P(vp)]
+    lib.siglip_encode.argtypes = [vp, vp, i32, vp, vp]
+    lib.siglip_attention.argtypes = [vp, vp, vp, i64, vp, i32, i32, i32, i32, ctypes.c_float, vp]
+    lib.siglip_destroy.argtypes = [vp]
+    lib.siglip_status_string.argtypes = [ctypes.c_int]
+    lib.siglip_status_string.restype = ctypes.c_char_p
+    lib.siglip_last_error.argtypes = []
+    lib.siglip_last_error.restype = ctypes.c_char_p
+    lib.siglip_model_info.argtypes = [vp] + [P(i32)] * 9
+    lib.siglip_debug_capture.argtypes = [vp, i32]
+    lib.siglip_debug_stage_info.argtypes = [vp, i32, P(i64), P(i64), P(i64), P(i32)]
+    lib.siglip_debug_stage.argtypes = [vp, i32, vp, ctypes.c_size_t]
+    lib.siglip_debug_fill_workspace.argtypes = [vp, ctypes.c_uint16]
+    for name in EXPORTED:
+        getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return load_library().siglip_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load_library().siglip_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != SIGLIP_OK:
+        raise SiglipError(status, last_error())
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _host_ptr(buf) -> tuple:
+    arr = np.frombuffer(buf, dtype=np.uint8)
+    return arr, arr.ctypes.data, arr.nbytes
+
+
+class Model:
+    """A resident encoder: weights uploaded once by siglip_create."""
+
+    def __init__(self, blob, layers: int = 0, max_batch: int = 1, fp8: bool = False,
+                 fp8_scale_exp: int = -4):
+        lib = load_library()
+        keep, ptr, n = _host_ptr(blob)
+        opt = siglip_options(layers, max_batch, 1 if fp8 else 0, fp8_scale_exp)
+        h = ctypes.c_void_p()
+        _check(lib.siglip_create(ptr, n, ctypes.byref(opt), ctypes.byref(h)))
+        self._h = h
+        del keep
+        vals = [ctypes.c_int32() for _ in range(9)]
+        _check(lib.siglip_model_info(self._h, *[ctypes.byref(v) for v in vals]))
+        (self.width, self.layers, self.heads, self.head_dim, self.mlp, self.tokens,
+         self.patch_dim, self.max_batch, prec) = [v.value for v in vals]
+        self.fp8 = prec == 1
+        self.fp8_scale_exp = fp8_scale_exp
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("model is closed")
+        return self._h
+
+    def encode(self, pixels, out=None, stream=None):
+        """pixels: CUDA float16 [B, tokens, patch_dim] -> float16 [B, 1, width]."""
+        import torch
+        if pixels.device.type != "cuda" or pixels.dtype != torch.float16 or not pixels.is_contiguous():
+            raise ValueError("pixels must be a contiguous CUDA float16 tensor")
+        if pixels.dim() != 3 or tuple(pixels.shape[1:]) != (self.tokens, self.patch_dim):
+            raise ValueError(f"pixels must be [B, {self.tokens}, {self.patch_dim}]")
+        b = pixels.shape[0]
+        if out is None:
+            out = torch.empty((b, 1, self.width), dtype=torch.float16, device=pixels.device)
+        elif (out.dtype != torch.float16 or not out.is_contiguous()
+              or tuple(out.shape) != (b, 1, self.width)):
+            raise ValueError("out must be a contiguous float16 [B, 1, width] tensor")
+        _check(load_library().siglip_encode(self.handle, pixels.data_ptr(), b, out.data_ptr(),
+                                            _stream_ptr(stream)))
+        return out
+
+    # ---- diagnostics
+    def debug_capture(self, layer: int) -> None:
+        _check(load_library().siglip_debug_capture(self.handle, layer))
+
+    def debug_stage_info(self, stage):
+        s = STAGE[stage] if isinstance(stage, str) else stage
+        r, c, l, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(load_library().siglip_debug_stage_info(self.handle, s, ctypes.byref(r), ctypes.byref(c),
+                                                      ctypes.byref(l), ctypes.byref(e)))
+        return r.value, c.value, l.value, e.value
+
+    def debug_stage(self, stage, full: bool = False) -> np.ndarray:
+        """Captured stage as a numpy array [rows, cols] ([rows, ld] with
+        full=True, padding columns included): float16, or uint8 e4m3 codes
+        (value = code * 2^fp8_scale_exp) for FP8 operand stages."""
+        s = STAGE[stage] if isinstance(stage, str) else stage
+        rows, cols, ld, eb = self.debug_stage_info(s)
+        buf = np.empty(rows * ld * eb, np.uint8)
+        _check(load_library().siglip_debug_stage(self.handle, s, buf.ctypes.data, buf.nbytes))
+        arr = buf.view(np.float16 if eb == 2 else np.uint8).reshape(rows, ld)
+        return arr if full else arr[:, :cols]
+
+    def debug_fill_workspace(self, pattern: int) -> None:
+        _check(load_library().siglip_debug_fill_workspace(self.handle, pattern))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            load_library().siglip_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def attention(q, k, v, heads: int, head_dim: int, scale: float, out=None, row_stride: Optional[int] = None,
+              tokens: Optional[int] = None, batch: Optional[int] = None, stream=None):
+    """siglip_attention on CUDA float16 tensors or views; q/k/v rows hold
+    heads*head_dim values at row_stride elements apart (default
+    heads*head_dim). batch and tokens default to q.shape[0] and q.shape[1]."""
+    import torch
+    b = batch if batch is not None else q.shape[0]
+    t = tokens if tokens is not None else q.shape[1]
+    w = heads * head_dim
+    if row_stride is None:
+        row_stride = w
+    if out is None:
+        out = torch.empty((b, t, w), dtype=torch.float16, device=q.device)
+    for x in (q, k, v, out):
+        if x.device.type != "cuda" or x.dtype != torch.float16:
+            raise ValueError("q, k, v, out must be CUDA float16")
+    _check(load_library().siglip_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_stride,
+                                           out.data_ptr(), b, heads, t, head_dim, float(scale),
+                                           _stream_ptr(stream)))
+    return out
+
+
+def e4m3_decode(codes: np.ndarray, scale_exp: int = -4) -> np.ndarray:
+    """Values of e4m3fn codes stored at scale 2^-scale_exp (test/diagnostic helper)."""
+    c = codes.astype(np.int32)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where((e == 0xF) & (m == 7), np.nan, v)
+    return s * v * 2.0 ** scale_exp

@@ -1,0 +1,302 @@
+// Attention kernels.
+//
+// flash_attn: encoder self-attention, softmax(Q K^T * scale) V per image and
+// head, T = 729 tokens, head width 72 (page "Single-layer SigLIP vision
+// benchmark", intro). Softmax state (running maximum, denominator) and the
+// accumulator stay F32 and the result is converted to F16 once (same page,
+// precision paragraph); the blocked/online merge of the pages' attention
+// (page "Capacity-first baseline", "Correctness fixes": running maximum and
+// denominator kept with each accumulator row) is done here in registers, so
+// no probability or score tensor is ever written to memory.
+//
+// Padding: head width 72 is padded to 80 for the QK contraction and to 96
+// for the PV output, keys to a multiple of 64, queries to a multiple of 128.
+// Every pad value is a zero written by this kernel into registers or LDS,
+// keys past T are masked to -inf before the maximum, so no data past token
+// T-1 of an image or column 71 of a head is ever read (the pages' PV-padding
+// NaN came from reading stale statistics as F16: page "SigLIP optimized
+// execution and PV padding", "Cause and fix").
+//
+// Work split: a workgroup of 4 waves takes 128 queries of one (image, head);
+// each wave owns 32 queries. Per block of 64 keys the workgroup stages K
+// [64 x 80] and V transposed [96 x 64] in LDS; each wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_f16 (keys on the MFMA rows, so every
+// lane holds 16 scores of ONE query and the row max / sum need one
+// cross-half shuffle), rescales, and computes O^T += V^T P^T where the P
+// fragment is the F32 score registers converted to F16 in place (the K
+// order inside a 16-key step is chosen to match the score layout, and V^T
+// is read in that same order).
+//
+// map_attn: MAP-head probe attention, one query per (image, head) against the
+// T encoder tokens (page "Single-layer SigLIP vision benchmark", intro: one
+// shared learned probe, its own query projection, one fused KV projection).
+// Memory-bound: it reads K and V once (2 x T x 72 x 2 bytes per head).
+#include "common.h"
+
+namespace siglip {
+namespace {
+
+constexpr int QB = 128;   // queries per workgroup
+constexpr int KB = 64;    // keys per block
+constexpr int KST = 88;   // K tile row stride in halfs (176 B: conflict-free 16-B reads)
+constexpr int VROWS = 96; // padded head width of the PV output (3 x 32)
+constexpr int VST = 68;   // V^T tile row stride in halfs (136 B)
+constexpr float kNegInf = -__builtin_inff();
+
+template <bool OUT_FP8>
+__global__ __launch_bounds__(256) void flash_attn_kernel(
+    const f16* __restrict__ q, const f16* __restrict__ k, const f16* __restrict__ v, int64_t ld,
+    void* __restrict__ o, int64_t ldo, int T, int D, float sl2, float out_scale) {
+  __shared__ __attribute__((aligned(16))) f16 Ks[KB * KST];
+  __shared__ __attribute__((aligned(16))) f16 Vt[VROWS * VST];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int fr = lane & 31;
+  const int fg = lane >> 5;
+  const int b = blockIdx.z;
+  const int hc = blockIdx.y * D;
+  const int64_t img = (int64_t)b * T;
+  const int qi = blockIdx.x * QB + wave * 32 + fr;  // this lane's query
+
+  // Q fragments: query qi, head dims 16s + 8fg .. +7 (zero past D and T)
+  f16x8 qf[5];
+#pragma unroll
+  for (int s = 0; s < 5; ++s) {
+    const int d0 = 16 * s + 8 * fg;
+    if (qi < T && d0 < D)
+      qf[s] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
+    else
+      qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  // V^T rows D..95 stay zero for the whole kernel
+  for (int i = t; i < (VROWS - D) * VST; i += 256) Vt[D * VST + i] = (f16)0.0f;
+
+  float m_run = kNegInf, l_run = 0.0f;
+  f32x16 oacc[3];
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+
+  const int nkb = (T + KB - 1) / KB;
+  const int vch = D >> 3;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int key0 = kb * KB;
+    __syncthreads();  // every wave is done reading the previous block
+    for (int c = t; c < KB * 10; c += 256) {
+      const int key = c / 10, ch = c % 10;
+      const int kk = key0 + key;
+      i32x4 val = {0, 0, 0, 0};
+      if (kk < T && ch * 8 < D) val = *reinterpret_cast<const i32x4*>(k + (img + kk) * ld + hc + ch * 8);
+      *reinterpret_cast<i32x4*>(&Ks[key * KST + ch * 8]) = val;
+    }
+    for (int c = t; c < KB * vch; c += 256) {
+      const int key = c / vch, ch = c % vch;
+      const int kk = key0 + key;
+      f16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (kk < T) val = *reinterpret_cast<const f16x8*>(v + (img + kk) * ld + hc + ch * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Vt[(ch * 8 + i) * VST + key] = val[i];
+    }
+    __syncthreads();
+
+    // S^T[key][query] for keys key0 + 32kt + (8(r/4) + 4fg + r%4)
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(&Ks[(32 * kt + fr) * KST + 16 * s + 8 * fg]);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3);
+        const float sv = key < T ? sacc[kt][r] * sl2 : kNegInf;
+        sacc[kt][r] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ls = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - m_new);
+        sacc[kt][r] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+    // O^T[d][query] += V^T[d][keys] P^T[keys][query], 16 keys per step; the
+    // lane group fg slots hold keys 16s + 4fg + (0..3) then 16s + 8 + 4fg + (0..3)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kt = s >> 1, base = 8 * (s & 1);
+      f16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = (f16)sacc[kt][base + e];
+#pragma unroll
+      for (int dt = 0; dt < 3; ++dt) {
+        const f16* vr = &Vt[(32 * dt + fr) * VST + 16 * s + 4 * fg];
+        const f16x4 lo = *reinterpret_cast<const f16x4*>(vr);
+        const f16x4 hi = *reinterpret_cast<const f16x4*>(vr + 8);
+        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  if (qi >= T) return;
+  const float inv = 1.0f / l_run;
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d0 = 32 * dt + 8 * qd + 4 * fg;
+      if (d0 >= D) continue;
+      const float a0 = oacc[dt][4 * qd + 0] * inv, a1 = oacc[dt][4 * qd + 1] * inv;
+      const float a2 = oacc[dt][4 * qd + 2] * inv, a3 = oacc[dt][4 * qd + 3] * inv;
+      if constexpr (OUT_FP8) {
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(o) + (img + qi) * ldo + hc + d0) =
+            pack4_e4m3(a0 * out_scale, a1 * out_scale, a2 * out_scale, a3 * out_scale);
+      } else {
+        const f16x4 ov = {(f16)a0, (f16)a1, (f16)a2, (f16)a3};
+        *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(o) + (img + qi) * ldo + hc + d0) = ov;
+      }
+    }
+}
+
+constexpr int kMapMaxT = 4096;
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <bool OUT_FP8>
+__global__ __launch_bounds__(256) void map_attn_kernel(
+    const f16* __restrict__ q, const f16* __restrict__ kv, int64_t ldkv, int64_t voff,
+    void* __restrict__ o, int64_t ldo, int T, int D, float sl2, float out_scale) {
+  __shared__ float sq[80];
+  __shared__ float sp[kMapMaxT];
+  __shared__ float red[4];
+  __shared__ float part[32][80];
+
+  const int t = threadIdx.x;
+  const int hc = blockIdx.x * D;
+  const int b = blockIdx.y;
+  const f16* base = kv + (int64_t)b * T * ldkv + hc;
+  if (t < D) sq[t] = (float)q[hc + t] * sl2;
+  __syncthreads();
+
+  const int nch = D >> 3;
+  float lmax = kNegInf;
+  for (int key = t; key < T; key += 256) {
+    const f16* kr = base + (int64_t)key * ldkv;
+    float s = 0.0f;
+    for (int ch = 0; ch < nch; ++ch) {
+      const f16x8 x = *reinterpret_cast<const f16x8*>(kr + 8 * ch);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += (float)x[i] * sq[8 * ch + i];
+    }
+    sp[key] = s;
+    lmax = fmaxf(lmax, s);
+  }
+  const float M = block_max(lmax, red);
+  float lsum = 0.0f;
+  for (int key = t; key < T; key += 256) {
+    const float p = __builtin_amdgcn_exp2f(sp[key] - M);
+    sp[key] = p;
+    lsum += p;
+  }
+  const float L = block_sum(lsum, red);  // includes a barrier: sp[] complete
+
+  const int ng = min(256 / nch, 32);
+  const int grp = t / nch, ch = t % nch;
+  if (grp < ng) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int key = grp; key < T; key += ng) {
+      const f16x8 x = *reinterpret_cast<const f16x8*>(base + (int64_t)key * ldkv + voff + 8 * ch);
+      const float p = sp[key];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += p * (float)x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[grp][8 * ch + i] = acc[i];
+  }
+  __syncthreads();
+  if (t < D) {
+    float s = 0.0f;
+    for (int g = 0; g < ng; ++g) s += part[g][t];
+    const float r = s / L;
+    if constexpr (OUT_FP8) {
+      reinterpret_cast<uint8_t*>(o)[(int64_t)b * ldo + hc + t] =
+          (uint8_t)(cvt_pk_e4m3(r * out_scale, 0.0f, 0u, false) & 0xFF);
+    } else {
+      reinterpret_cast<f16*>(o)[(int64_t)b * ldo + hc + t] = (f16)r;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v, int64_t ld, void* o,
+                                  int64_t ldo, int batch, int heads, int tokens, int head_dim,
+                                  float scale, bool out_fp8, float out_scale, hipStream_t s) {
+  if (batch < 1 || heads < 1 || tokens < 1 || head_dim < 8 || head_dim > 80 || (head_dim & 7) ||
+      ld < (int64_t)heads * head_dim || (ld & 7) || ldo < (int64_t)heads * head_dim || (ldo & 3))
+    return hipErrorInvalidValue;
+  if (batch > 65535 || heads > 65535) return hipErrorInvalidValue;
+  const float sl2 = scale * 1.4426950408889634f;
+  dim3 grid((tokens + QB - 1) / QB, heads, batch);
+  if (out_fp8)
+    hipLaunchKernelGGL(flash_attn_kernel<true>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, sl2, out_scale);
+  else
+    hipLaunchKernelGGL(flash_attn_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, sl2, out_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv, int64_t v_offset, void* o,
+                                int64_t ldo, int batch, int heads, int tokens, int head_dim,
+                                float scale, bool out_fp8, float out_scale, hipStream_t s) {
+  if (batch < 1 || heads < 1 || tokens < 1 || tokens > kMapMaxT || head_dim < 8 || head_dim > 80 ||
+      (head_dim & 7) || (ldkv & 7) || (v_offset & 7) || batch > 65535)
+    return hipErrorInvalidValue;
+  const float sl2 = scale * 1.4426950408889634f;
+  dim3 grid(heads, batch);
+  if (out_fp8)
+    hipLaunchKernelGGL(map_attn_kernel<true>, grid, dim3(256), 0, s, q, kv, ldkv, v_offset, o, ldo, tokens, head_dim, sl2, out_scale);
+  else
+    hipLaunchKernelGGL(map_attn_kernel<false>, grid, dim3(256), 0, s, q, kv, ldkv, v_offset, o, ldo, tokens, head_dim, sl2, out_scale);
+  return hipGetLastError();
+}
+
+}  // namespace siglip

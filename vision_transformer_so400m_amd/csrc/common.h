@@ -1,0 +1,123 @@
+// Internal declarations shared by the HIP sources of libsiglip (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+namespace siglip {
+
+constexpr float kE4m3Max = 448.0f;
+
+// Two floats -> two OCP e4m3fn codes (round to nearest even) packed into the
+// low (hi=false) or high (hi=true) 16 bits of `old`. Inputs are clamped to
+// +-448 first so out-of-range values saturate instead of becoming NaN.
+__device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b, uint32_t old, bool hi) {
+  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
+  b = fminf(fmaxf(b, -kE4m3Max), kE4m3Max);
+  return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
+            : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
+}
+
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  uint32_t w = cvt_pk_e4m3(a, b, 0u, false);
+  return cvt_pk_e4m3(c, d, w, true);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
+// tanh(u) = 1 - 2 / (exp(2u) + 1) evaluated through exp2.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k2 = 2.0f * 0.7978845608028654f * 1.4426950408889634f;  // 2*sqrt(2/pi)*log2(e)
+  float u = x + 0.044715f * x * x * x;
+  float e = __builtin_amdgcn_exp2f(k2 * u);   // exp(2*sqrt(2/pi)*u)
+  float t = 1.0f - 2.0f / (e + 1.0f);         // saturates to +-1 for large |u|
+  return 0.5f * x * (1.0f + t);
+}
+
+// ------------------------------------------------------------------ GEMM
+// C[M, N] = epilogue(A[M, K] . Wt[N, K]^T). A and Wt are K-contiguous, either
+// both F16 or both e4m3 codes. K is a multiple of 128 bytes of A row, N a
+// multiple of the chosen column tile (weights are padded at create time).
+enum GemmEpi : int {
+  EPI_BIAS = 0,      // acc*s + bias[n]
+  EPI_BIAS_POS = 1,  // acc*s + bias[n] + pos[m % pos_rows][n]
+  EPI_BIAS_RES = 2,  // acc*s + bias[n] + res[m][n]
+  EPI_BIAS_GELU = 3  // gelu(acc*s + bias[n])
+};
+
+struct GemmArgs {
+  const void* a; int64_t lda;     // elements
+  const void* w; int64_t ldw;     // elements (row n of Wt)
+  void* c; int64_t ldc;           // elements of the output type
+  const float* bias;              // [N]
+  const float* pos; int pos_rows; int64_t ldpos;
+  const f16* res; int64_t ldres;
+  int M, N, K;                    // K in elements
+  float acc_scale;                // 1 (F16) or 2^(2*exp) (FP8)
+  float out_scale;                // for e4m3 outputs: 2^-exp
+};
+
+hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8,
+                       hipStream_t s);
+
+// ------------------------------------------------------------- LayerNorm
+hipError_t launch_layernorm(const f16* x, int64_t ldx, void* y, int64_t ldy,
+                            const float* gamma, const float* beta, int rows,
+                            int width, float eps, bool out_fp8, float out_scale,
+                            hipStream_t s);
+
+// ------------------------------------------------------------- attention
+hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v,
+                                  int64_t ld, void* o, int64_t ldo, int batch,
+                                  int heads, int tokens, int head_dim,
+                                  float scale, bool out_fp8, float out_scale,
+                                  hipStream_t s);
+
+hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv,
+                                int64_t v_offset, void* o, int64_t ldo,
+                                int batch, int heads, int tokens, int head_dim,
+                                float scale, bool out_fp8, float out_scale,
+                                hipStream_t s);
+
+// ------------------------------------------------------------ conversion
+// F16 [rows, cols] (row stride ldx) -> [rows, cols_pad] F16 or e4m3 codes of
+// x*scale, columns cols..cols_pad-1 set to zero.
+hipError_t launch_pad_convert(const f16* x, int64_t ldx, void* y, int rows,
+                              int cols, int cols_pad, bool out_fp8, float scale,
+                              hipStream_t s);
+
+// F32 weight [K, N] -> Wt [N_pad, K_pad] (F16 or e4m3 codes of w*scale),
+// zero in the padding.
+hipError_t launch_weight_transpose(const float* w, int K, int N, void* wt,
+                                   int K_pad, int N_pad, bool out_fp8,
+                                   float scale, hipStream_t s);
+
+// F32 [rows, cols] -> [rows, cols_pad] F16 or e4m3 codes of x*scale.
+hipError_t launch_f32_convert(const float* x, int rows, int cols, void* y,
+                              int cols_pad, bool out_fp8, float scale,
+                              hipStream_t s);
+
+// Fill n 16-bit words.
+hipError_t launch_fill_u16(void* p, size_t n, uint16_t value, hipStream_t s);
+
+}  // namespace siglip

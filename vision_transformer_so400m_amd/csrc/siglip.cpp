@@ -1,0 +1,647 @@
+// libsiglip: C ABI, weight-blob parsing, resident weights, workspace and the
+// per-call kernel sequence of the SigLIP So400m/14 image encoder on one
+// gfx950 GPU. The sequence follows the page "Single-layer SigLIP vision
+// benchmark" (intro and mermaid figure):
+//
+//   X [B*T, 588] --pad/convert--> Xp [B*T, 640]
+//   H = Xp Wpe + bpe + pos[t]                      (GEMM, EPI_BIAS_POS)
+//   per layer:  A = LN1(H)                         (layernorm)
+//               QKV = A Wqkv + b                   (GEMM, EPI_BIAS)
+//               O = attention(QKV views)           (flash attention)
+//               H = O Wo + bo + H                  (GEMM, EPI_BIAS_RES, in place)
+//               A = LN2(H)
+//               U = gelu(A W1 + b1)                (GEMM, EPI_BIAS_GELU)
+//               H = U W2 + b2 + H                  (GEMM, EPI_BIAS_RES)
+//   Z = LN(H); KV = Z Wkv + bkv; o = probe-attention(q, KV)
+//   y = o Wo' + bo'; out = gelu(LN(y) W1' + b1') W2' + b2' + y
+//
+// The probe query q = probe Wq + bq is image-independent ("Each batch uses the
+// same learned probe") and is computed once at create time by the same GEMM.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/siglip.h"
+#include "common.h"
+
+using namespace siglip;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+struct HipFail {
+  hipError_t err;
+  std::string where;
+};
+
+void hip_check(hipError_t e, const char* where) {
+  if (e != hipSuccess) throw HipFail{e, where};
+}
+
+struct BadBlob {
+  std::string msg;
+};
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int kKAlign = 128;  // K padding (elements): whole 128-byte slices for both F16 and e4m3
+constexpr int kNAlign = 128;  // N padding: the widest GEMM column tile
+
+struct Gemm {
+  void* w = nullptr;      // [n_pad, k_pad] F16 or e4m3, K-contiguous
+  float* bias = nullptr;  // [n_pad]
+  int k = 0, n = 0, k_pad = 0, n_pad = 0;
+};
+
+struct Layer {
+  float *ln1_g, *ln1_b, *ln2_g, *ln2_b;
+  Gemm qkv, out, mlp1, mlp2;
+};
+
+struct BlobHeader {
+  char magic[4];
+  uint32_t version, width, depth, heads, head_dim, mlp, tokens, patch_dim, dtype;
+  uint64_t total_bytes;
+  uint8_t reserved[16];
+};
+static_assert(sizeof(BlobHeader) == 64, "blob header is 64 bytes");
+
+struct TensorRef {
+  const float* host;
+  int64_t rows, cols;
+};
+
+// Walks the blob in canonical order, checking bounds.
+class BlobReader {
+ public:
+  BlobReader(const uint8_t* base, size_t size) : base_(base), size_(size), off_(64) {}
+  TensorRef next(const char* name, int64_t rows, int64_t cols) {
+    off_ = (size_t)round_up((int64_t)off_, 64);
+    const size_t n = (size_t)(rows * cols) * 4;
+    if (off_ + n > size_) throw BadBlob{std::string("blob truncated at tensor ") + name};
+    TensorRef r{reinterpret_cast<const float*>(base_ + off_), rows, cols};
+    off_ += n;
+    return r;
+  }
+  size_t end() const { return (size_t)round_up((int64_t)off_, 64); }
+
+ private:
+  const uint8_t* base_;
+  size_t size_;
+  size_t off_;
+};
+
+}  // namespace
+
+struct siglip_model {
+  int device = 0;
+  int width = 0, depth = 0, layers = 0, heads = 0, head_dim = 0, mlp = 0, tokens = 0, patch_dim = 0;
+  int max_batch = 0;
+  bool fp8 = false;
+  int scale_exp = 0;
+  float op_scale = 1.0f;   // operand quantization multiplier 2^-exp
+  float acc_scale = 1.0f;  // product rescale 2^(2 exp)
+  int patch_pad = 0, mlp_pad = 0;
+
+  std::vector<void*> allocs;
+  Gemm embed;
+  float* pos = nullptr;
+  std::vector<Layer> L;
+  float *lnf_g = nullptr, *lnf_b = nullptr;
+  Gemm mq, mkv, mout, mmlp1, mmlp2;
+  float *mln_g = nullptr, *mln_b = nullptr;
+  f16* map_q = nullptr;  // [width]
+
+  // workspace
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  void* xp = nullptr;   // [M, patch_pad] operand type
+  f16* h = nullptr;     // [M, width]
+  void* a = nullptr;    // [M, width] operand type
+  f16* qkv = nullptr;   // [M, 3 width] (also the MAP KV [M, 2 width])
+  void* o = nullptr;    // [M, width] operand type
+  void* u = nullptr;    // [M, mlp_pad] operand type
+  void* mo = nullptr;   // [B, width] operand type
+  f16* my = nullptr;    // [B, width]
+  void* ma = nullptr;   // [B, width] operand type
+  void* mu = nullptr;   // [B, mlp_pad] operand type
+
+  // diagnostics
+  int capture_layer = -1;
+  bool captured = false;
+  int captured_batch = 0;
+  void* cap[SIGLIP_STAGE_COUNT] = {};
+  size_t cap_bytes[SIGLIP_STAGE_COUNT] = {};
+
+  ~siglip_model() {
+    for (void* p : allocs) (void)hipFree(p);
+  }
+
+  int esz() const { return fp8 ? 1 : 2; }
+
+  void* dalloc(size_t bytes) {
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, std::max<size_t>(bytes, 256));
+    if (e != hipSuccess) throw HipFail{e, "hipMalloc"};
+    allocs.push_back(p);
+    return p;
+  }
+};
+
+namespace {
+
+float* upload_f32(siglip_model* m, const TensorRef& t, int64_t pad_to = 0) {
+  const int64_t n = t.rows * t.cols;
+  const int64_t np = std::max(n, pad_to);
+  float* d = static_cast<float*>(m->dalloc((size_t)np * 4));
+  if (np > n) hip_check(hipMemset(d, 0, (size_t)np * 4), "hipMemset");
+  hip_check(hipMemcpy(d, t.host, (size_t)n * 4, hipMemcpyHostToDevice), "hipMemcpy");
+  return d;
+}
+
+// weight [k, n] F32 (host) -> resident [n_pad, k_pad] operand type + F32 bias
+Gemm make_gemm(siglip_model* m, const TensorRef& w, const TensorRef& b, float* staging) {
+  Gemm g;
+  g.k = (int)w.rows;
+  g.n = (int)w.cols;
+  g.k_pad = (int)round_up(g.k, kKAlign);
+  g.n_pad = (int)round_up(g.n, kNAlign);
+  g.w = m->dalloc((size_t)g.n_pad * g.k_pad * m->esz());
+  hip_check(hipMemcpy(staging, w.host, (size_t)g.k * g.n * 4, hipMemcpyHostToDevice), "hipMemcpy");
+  hip_check(launch_weight_transpose(staging, g.k, g.n, g.w, g.k_pad, g.n_pad, m->fp8, m->fp8 ? m->op_scale : 1.0f, nullptr),
+            "weight_transpose");
+  hip_check(hipDeviceSynchronize(), "weight_transpose sync");
+  g.bias = upload_f32(m, b, g.n_pad);
+  return g;
+}
+
+void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, void* c, int64_t ldc, int epi,
+          bool out_fp8, const f16* res, int64_t ldres, hipStream_t s) {
+  GemmArgs args{};
+  args.a = a;
+  args.lda = lda;
+  args.w = g.w;
+  args.ldw = g.k_pad;
+  args.c = c;
+  args.ldc = ldc;
+  args.bias = g.bias;
+  args.pos = m->pos;
+  args.pos_rows = m->tokens;
+  args.ldpos = m->width;
+  args.res = res;
+  args.ldres = ldres;
+  args.M = M;
+  args.N = g.n_pad;
+  args.K = g.k_pad;
+  args.acc_scale = m->acc_scale;
+  args.out_scale = m->op_scale;
+  hip_check(launch_gemm(args, epi, m->fp8, out_fp8, s), "gemm launch");
+}
+
+void capture(siglip_model* m, int stage, const void* src, size_t bytes, hipStream_t s) {
+  if (m->capture_layer < 0 || !m->cap[stage]) return;
+  hip_check(hipMemcpyAsync(m->cap[stage], src, bytes, hipMemcpyDeviceToDevice, s), "capture copy");
+}
+
+void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int64_t* cols, int64_t* ld,
+                 int32_t* eb) {
+  const int64_t M = (int64_t)batch * m->tokens;
+  const int e = m->esz();
+  int64_t r = M, c = m->width, l = m->width;
+  int32_t b = 2;
+  switch (stage) {
+    case SIGLIP_STAGE_EMBED: case SIGLIP_STAGE_H_ATTN: case SIGLIP_STAGE_H_OUT: break;
+    case SIGLIP_STAGE_LN1: case SIGLIP_STAGE_ATTN: case SIGLIP_STAGE_LN2: case SIGLIP_STAGE_FINAL_LN: b = e; break;
+    case SIGLIP_STAGE_QKV: c = l = 3LL * m->width; break;
+    case SIGLIP_STAGE_MLP_HIDDEN: c = m->mlp; l = m->mlp_pad; b = e; break;
+    case SIGLIP_STAGE_MAP_KV: c = l = 2LL * m->width; break;
+    case SIGLIP_STAGE_MAP_ATTN: case SIGLIP_STAGE_MAP_LN: r = batch; b = e; break;
+    case SIGLIP_STAGE_MAP_Y: r = batch; break;
+    case SIGLIP_STAGE_MAP_HIDDEN: r = batch; c = m->mlp; l = m->mlp_pad; b = e; break;
+    case SIGLIP_STAGE_MAP_Q: r = 1; break;
+  }
+  if (rows) *rows = r;
+  if (cols) *cols = c;
+  if (ld) *ld = l;
+  if (eb) *eb = b;
+}
+
+void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) {
+  const int M = B * m->tokens;
+  const int W = m->width;
+  const int e = m->esz();
+  const bool q8 = m->fp8;
+  const bool cap = m->capture_layer >= 0;
+  auto cb = [&](int stage) {
+    int64_t r, c, l;
+    int32_t b;
+    stage_shape(m, stage, B, &r, &c, &l, &b);
+    return (size_t)(r * l * b);
+  };
+
+  hip_check(launch_pad_convert(x, m->patch_dim, m->xp, M, m->patch_dim, m->patch_pad, q8, q8 ? m->op_scale : 1.0f, s),
+            "pad_convert");
+  gemm(m, m->embed, m->xp, m->patch_pad, M, m->h, W, EPI_BIAS_POS, false, nullptr, 0, s);
+  if (cap) capture(m, SIGLIP_STAGE_EMBED, m->h, cb(SIGLIP_STAGE_EMBED), s);
+
+  const float attn_scale = 1.0f / std::sqrt((float)m->head_dim);
+  for (int i = 0; i < m->layers; ++i) {
+    const Layer& Ly = m->L[i];
+    const bool ci = cap && i == m->capture_layer;
+    hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
+    if (ci) capture(m, SIGLIP_STAGE_LN1, m->a, cb(SIGLIP_STAGE_LN1), s);
+    gemm(m, Ly.qkv, m->a, W, M, m->qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    if (ci) capture(m, SIGLIP_STAGE_QKV, m->qkv, cb(SIGLIP_STAGE_QKV), s);
+    hip_check(launch_flash_attention(m->qkv, m->qkv + W, m->qkv + 2 * W, 3 * W, m->o, W, B, m->heads, m->tokens,
+                                     m->head_dim, attn_scale, q8, m->op_scale, s),
+              "attention");
+    if (ci) capture(m, SIGLIP_STAGE_ATTN, m->o, cb(SIGLIP_STAGE_ATTN), s);
+    gemm(m, Ly.out, m->o, W, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+    if (ci) capture(m, SIGLIP_STAGE_H_ATTN, m->h, cb(SIGLIP_STAGE_H_ATTN), s);
+    hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
+    if (ci) capture(m, SIGLIP_STAGE_LN2, m->a, cb(SIGLIP_STAGE_LN2), s);
+    gemm(m, Ly.mlp1, m->a, W, M, m->u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+    if (ci) capture(m, SIGLIP_STAGE_MLP_HIDDEN, m->u, cb(SIGLIP_STAGE_MLP_HIDDEN), s);
+    gemm(m, Ly.mlp2, m->u, m->mlp_pad, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+    if (ci) capture(m, SIGLIP_STAGE_H_OUT, m->h, cb(SIGLIP_STAGE_H_OUT), s);
+  }
+
+  hip_check(launch_layernorm(m->h, W, m->a, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, q8, m->op_scale, s), "final ln");
+  if (cap) capture(m, SIGLIP_STAGE_FINAL_LN, m->a, cb(SIGLIP_STAGE_FINAL_LN), s);
+  f16* kv = m->qkv;  // [M, 2W]
+  gemm(m, m->mkv, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_KV, kv, cb(SIGLIP_STAGE_MAP_KV), s);
+  hip_check(launch_map_attention(m->map_q, kv, 2 * W, W, m->mo, W, B, m->heads, m->tokens, m->head_dim, attn_scale,
+                                 q8, m->op_scale, s),
+            "map attention");
+  if (cap) capture(m, SIGLIP_STAGE_MAP_ATTN, m->mo, cb(SIGLIP_STAGE_MAP_ATTN), s);
+  gemm(m, m->mout, m->mo, W, B, m->my, W, EPI_BIAS, false, nullptr, 0, s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_Y, m->my, cb(SIGLIP_STAGE_MAP_Y), s);
+  hip_check(launch_layernorm(m->my, W, m->ma, W, m->mln_g, m->mln_b, B, W, 1e-6f, q8, m->op_scale, s), "map ln");
+  if (cap) capture(m, SIGLIP_STAGE_MAP_LN, m->ma, cb(SIGLIP_STAGE_MAP_LN), s);
+  gemm(m, m->mmlp1, m->ma, W, B, m->mu, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_HIDDEN, m->mu, cb(SIGLIP_STAGE_MAP_HIDDEN), s);
+  gemm(m, m->mmlp2, m->mu, m->mlp_pad, B, out, W, EPI_BIAS_RES, false, m->my, W, s);
+  if (cap) {
+    m->captured = true;
+    m->captured_batch = B;
+  }
+}
+
+int validate_header(const BlobHeader& h, size_t blob_bytes, std::string* why) {
+  if (std::memcmp(h.magic, "SGLP", 4) != 0) return (*why = "bad magic (expected \"SGLP\")", SIGLIP_E_BAD_BLOB);
+  if (h.version != 1) return (*why = "unsupported blob version " + std::to_string(h.version), SIGLIP_E_BAD_BLOB);
+  if (h.dtype != 0) return (*why = "unsupported blob dtype (only 0 = F32)", SIGLIP_E_BAD_BLOB);
+  if (h.width == 0 || h.depth == 0 || h.heads == 0 || h.head_dim == 0 || h.mlp == 0 || h.tokens == 0 ||
+      h.patch_dim == 0)
+    return (*why = "zero dimension in blob header", SIGLIP_E_BAD_BLOB);
+  if (h.width > 16384 || h.depth > 1024 || h.mlp > 65536 || h.tokens > 65536 || h.patch_dim > 65536)
+    return (*why = "implausible dimension in blob header", SIGLIP_E_BAD_BLOB);
+  if ((uint64_t)h.heads * h.head_dim != h.width)
+    return (*why = "width != heads * head_dim", SIGLIP_E_BAD_BLOB);
+  if (h.total_bytes != blob_bytes)
+    return (*why = "blob size " + std::to_string(blob_bytes) + " != header total_bytes " +
+                   std::to_string(h.total_bytes), SIGLIP_E_BAD_BLOB);
+  return SIGLIP_OK;
+}
+
+int check_supported(const BlobHeader& h, std::string* why) {
+  // activation rows are GEMM operands read in whole 128-element K slices
+  if (h.width % 128) return (*why = "width must be a multiple of 128", SIGLIP_E_UNSUPPORTED);
+  if (h.width > 2048) return (*why = "width above 2048", SIGLIP_E_UNSUPPORTED);
+  if (h.head_dim % 8 || h.head_dim > 80) return (*why = "head_dim must be a multiple of 8 and <= 80", SIGLIP_E_UNSUPPORTED);
+  if (h.mlp % 8) return (*why = "mlp must be a multiple of 8", SIGLIP_E_UNSUPPORTED);
+  if (h.patch_dim % 4) return (*why = "patch_dim must be a multiple of 4", SIGLIP_E_UNSUPPORTED);
+  if (h.tokens > 4096) return (*why = "more than 4096 tokens", SIGLIP_E_UNSUPPORTED);
+  return SIGLIP_OK;
+}
+
+int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, siglip_model** out) {
+  if (!out) return fail(SIGLIP_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!blob || !opt) return fail(SIGLIP_E_INVALID_ARG, "blob or opt is NULL");
+  if (opt->max_batch < 1 || opt->max_batch > 4096) return fail(SIGLIP_E_INVALID_ARG, "max_batch must be 1..4096");
+  if (opt->gemm_precision != 0 && opt->gemm_precision != 1)
+    return fail(SIGLIP_E_INVALID_ARG, "gemm_precision must be 0 (F16) or 1 (FP8)");
+  if (opt->gemm_precision == 1 && (opt->fp8_scale_exp < -8 || opt->fp8_scale_exp > 8))
+    return fail(SIGLIP_E_INVALID_ARG, "fp8_scale_exp must be in -8..8");
+  if (blob_bytes < sizeof(BlobHeader)) return fail(SIGLIP_E_BAD_BLOB, "blob shorter than its 64-byte header");
+  BlobHeader h;
+  std::memcpy(&h, blob, sizeof h);
+  std::string why;
+  int st = validate_header(h, blob_bytes, &why);
+  if (st != SIGLIP_OK) return fail(st, why);
+  if (opt->layers < 0 || (uint32_t)opt->layers > h.depth)
+    return fail(SIGLIP_E_INVALID_ARG, "layers must be 0 (all) or 1..depth");
+  st = check_supported(h, &why);
+  if (st != SIGLIP_OK) return fail(st, why);
+
+  // Walk the whole blob once on the CPU before touching the GPU.
+  const int W = (int)h.width, F = (int)h.mlp, T = (int)h.tokens, P = (int)h.patch_dim;
+  BlobReader rd(static_cast<const uint8_t*>(blob), blob_bytes);
+  struct LayerRefs {
+    TensorRef ln1g, ln1b, qkvw, qkvb, outw, outb, ln2g, ln2b, m1w, m1b, m2w, m2b;
+  };
+  std::vector<LayerRefs> lr;
+  TensorRef ew, eb, pos, lfg, lfb, probe, qw, qb, kvw, kvb, ow, ob, mlg, mlb, m1w, m1b, m2w, m2b;
+  try {
+    ew = rd.next("embed.w", P, W);
+    eb = rd.next("embed.b", 1, W);
+    pos = rd.next("pos", T, W);
+    for (uint32_t i = 0; i < h.depth; ++i) {
+      LayerRefs r;
+      r.ln1g = rd.next("ln1.g", 1, W);
+      r.ln1b = rd.next("ln1.b", 1, W);
+      r.qkvw = rd.next("qkv.w", W, 3 * W);
+      r.qkvb = rd.next("qkv.b", 1, 3 * W);
+      r.outw = rd.next("out.w", W, W);
+      r.outb = rd.next("out.b", 1, W);
+      r.ln2g = rd.next("ln2.g", 1, W);
+      r.ln2b = rd.next("ln2.b", 1, W);
+      r.m1w = rd.next("mlp1.w", W, F);
+      r.m1b = rd.next("mlp1.b", 1, F);
+      r.m2w = rd.next("mlp2.w", F, W);
+      r.m2b = rd.next("mlp2.b", 1, W);
+      lr.push_back(r);
+    }
+    lfg = rd.next("final_ln.g", 1, W);
+    lfb = rd.next("final_ln.b", 1, W);
+    probe = rd.next("map.probe", 1, W);
+    qw = rd.next("map.q.w", W, W);
+    qb = rd.next("map.q.b", 1, W);
+    kvw = rd.next("map.kv.w", W, 2 * W);
+    kvb = rd.next("map.kv.b", 1, 2 * W);
+    ow = rd.next("map.out.w", W, W);
+    ob = rd.next("map.out.b", 1, W);
+    mlg = rd.next("map.ln.g", 1, W);
+    mlb = rd.next("map.ln.b", 1, W);
+    m1w = rd.next("map.mlp1.w", W, F);
+    m1b = rd.next("map.mlp1.b", 1, F);
+    m2w = rd.next("map.mlp2.w", F, W);
+    m2b = rd.next("map.mlp2.b", 1, W);
+  } catch (const BadBlob& b) {
+    return fail(SIGLIP_E_BAD_BLOB, b.msg);
+  }
+  if (rd.end() != blob_bytes) return fail(SIGLIP_E_BAD_BLOB, "blob has trailing bytes beyond its last tensor");
+
+  // Device checks.
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(SIGLIP_E_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", this build targets gfx950");
+
+  siglip_model* m = new (std::nothrow) siglip_model();
+  if (!m) return fail(SIGLIP_E_OUT_OF_MEMORY, "host allocation failed");
+  try {
+    m->device = dev;
+    m->width = W;
+    m->depth = (int)h.depth;
+    m->layers = opt->layers == 0 ? (int)h.depth : opt->layers;
+    m->heads = (int)h.heads;
+    m->head_dim = (int)h.head_dim;
+    m->mlp = F;
+    m->tokens = T;
+    m->patch_dim = P;
+    m->max_batch = opt->max_batch;
+    m->fp8 = opt->gemm_precision == 1;
+    m->scale_exp = m->fp8 ? opt->fp8_scale_exp : 0;
+    m->op_scale = std::ldexp(1.0f, -m->scale_exp);
+    m->acc_scale = std::ldexp(1.0f, 2 * m->scale_exp);
+    m->patch_pad = (int)round_up(P, kKAlign);
+    m->mlp_pad = (int)round_up(F, kNAlign);  // U is both an N (MLP up) and a K (MLP down) dimension
+
+    const size_t staging_floats = (size_t)std::max<int64_t>({(int64_t)P * W, 3LL * W * W, (int64_t)W * F, (int64_t)T * W});
+    float* staging = static_cast<float*>(m->dalloc(staging_floats * 4));
+
+    m->embed = make_gemm(m, ew, eb, staging);
+    m->pos = upload_f32(m, pos);
+    for (int i = 0; i < m->layers; ++i) {
+      const LayerRefs& r = lr[i];
+      Layer Ly;
+      Ly.ln1_g = upload_f32(m, r.ln1g);
+      Ly.ln1_b = upload_f32(m, r.ln1b);
+      Ly.ln2_g = upload_f32(m, r.ln2g);
+      Ly.ln2_b = upload_f32(m, r.ln2b);
+      Ly.qkv = make_gemm(m, r.qkvw, r.qkvb, staging);
+      Ly.out = make_gemm(m, r.outw, r.outb, staging);
+      Ly.mlp1 = make_gemm(m, r.m1w, r.m1b, staging);
+      Ly.mlp2 = make_gemm(m, r.m2w, r.m2b, staging);
+      m->L.push_back(Ly);
+    }
+    m->lnf_g = upload_f32(m, lfg);
+    m->lnf_b = upload_f32(m, lfb);
+    m->mq = make_gemm(m, qw, qb, staging);
+    m->mkv = make_gemm(m, kvw, kvb, staging);
+    m->mout = make_gemm(m, ow, ob, staging);
+    m->mmlp1 = make_gemm(m, m1w, m1b, staging);
+    m->mmlp2 = make_gemm(m, m2w, m2b, staging);
+    m->mln_g = upload_f32(m, mlg);
+    m->mln_b = upload_f32(m, mlb);
+
+    // workspace
+    const int64_t M = (int64_t)m->max_batch * T;
+    const int64_t B = m->max_batch;
+    const int es = m->esz();
+    struct Part { void** dst; int64_t bytes; };
+    std::vector<Part> parts = {
+        {&m->xp, M * m->patch_pad * es}, {(void**)&m->h, M * W * 2}, {&m->a, M * W * es},
+        {(void**)&m->qkv, M * 3 * W * 2}, {&m->o, M * W * es}, {&m->u, M * m->mlp_pad * es},
+        {&m->mo, B * W * es}, {(void**)&m->my, B * W * 2}, {&m->ma, B * W * es}, {&m->mu, B * m->mlp_pad * es},
+    };
+    size_t total = 0;
+    for (auto& p : parts) total += (size_t)round_up(p.bytes, 256);
+    m->ws = m->dalloc(total);
+    m->ws_bytes = total;
+    size_t off = 0;
+    for (auto& p : parts) {
+      *p.dst = static_cast<uint8_t*>(m->ws) + off;
+      off += (size_t)round_up(p.bytes, 256);
+    }
+
+    // probe query, once: q = probe Wq + bq (same GEMM as every projection)
+    void* probe_op = m->dalloc((size_t)m->mq.k_pad * es);
+    hip_check(hipMemcpy(staging, probe.host, (size_t)W * 4, hipMemcpyHostToDevice), "hipMemcpy");
+    hip_check(launch_f32_convert(staging, 1, W, probe_op, m->mq.k_pad, m->fp8, m->fp8 ? m->op_scale : 1.0f, nullptr),
+              "probe convert");
+    m->map_q = static_cast<f16*>(m->dalloc((size_t)m->mq.n_pad * 2));
+    gemm(m, m->mq, probe_op, m->mq.k_pad, 1, m->map_q, m->mq.n_pad, EPI_BIAS, false, nullptr, 0, nullptr);
+    hip_check(hipDeviceSynchronize(), "create sync");
+  } catch (const HipFail& f) {
+    delete m;
+    const int code = (f.err == hipErrorOutOfMemory || f.err == hipErrorMemoryAllocation) ? SIGLIP_E_OUT_OF_MEMORY
+                                                                                           : SIGLIP_E_HIP;
+    return fail(code, f.where + ": " + hipGetErrorString(f.err));
+  } catch (const std::bad_alloc&) {
+    delete m;
+    return fail(SIGLIP_E_OUT_OF_MEMORY, "host allocation failed");
+  }
+  *out = m;
+  return SIGLIP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+SIGLIP_API int siglip_create(const void* blob, size_t blob_bytes, const siglip_options* opt, siglip_model** out) {
+  try {
+    g_last_error.clear();
+    return create_impl(blob, blob_bytes, opt, out);
+  } catch (const std::exception& ex) {
+    return fail(SIGLIP_E_HIP, std::string("unexpected: ") + ex.what());
+  } catch (...) {
+    return fail(SIGLIP_E_HIP, "unexpected exception");
+  }
+}
+
+SIGLIP_API int siglip_encode(siglip_model* m, const void* pixels_f16, int32_t batch, void* out_f16, void* hip_stream) {
+  if (!m || !pixels_f16 || !out_f16) return fail(SIGLIP_E_INVALID_ARG, "null model, input or output pointer");
+  if (batch < 1 || batch > m->max_batch)
+    return fail(SIGLIP_E_INVALID_ARG, "batch " + std::to_string(batch) + " outside 1..max_batch (" +
+                                          std::to_string(m->max_batch) + ")");
+  if ((reinterpret_cast<uintptr_t>(pixels_f16) & 7) || (reinterpret_cast<uintptr_t>(out_f16) & 7))
+    return fail(SIGLIP_E_INVALID_ARG, "input and output must be 8-byte aligned");
+  try {
+    encode_impl(m, static_cast<const f16*>(pixels_f16), batch, static_cast<f16*>(out_f16),
+                static_cast<hipStream_t>(hip_stream));
+  } catch (const HipFail& f) {
+    return fail(SIGLIP_E_HIP, f.where + ": " + hipGetErrorString(f.err));
+  } catch (...) {
+    return fail(SIGLIP_E_HIP, "unexpected exception");
+  }
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_attention(const void* q, const void* k, const void* v, int64_t row_stride_elems, void* o,
+                                int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim, float scale,
+                                void* hip_stream) {
+  if (!q || !k || !v || !o) return fail(SIGLIP_E_INVALID_ARG, "null q, k, v or o");
+  if (batch < 1 || heads < 1 || tokens < 1 || batch > 65535 || heads > 65535)
+    return fail(SIGLIP_E_INVALID_ARG, "batch, heads and tokens must be >= 1 (batch, heads <= 65535)");
+  if (head_dim < 8 || head_dim > 80 || head_dim % 8)
+    return fail(SIGLIP_E_UNSUPPORTED, "head_dim must be a multiple of 8 in 8..80");
+  if (row_stride_elems < (int64_t)heads * head_dim || row_stride_elems % 8)
+    return fail(SIGLIP_E_INVALID_ARG, "row_stride_elems must be >= heads*head_dim and a multiple of 8");
+  for (const void* p : {q, k, v, (const void*)o})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(SIGLIP_E_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(SIGLIP_E_INVALID_ARG, "scale must be finite and > 0");
+  hipError_t e = launch_flash_attention(static_cast<const f16*>(q), static_cast<const f16*>(k),
+                                        static_cast<const f16*>(v), row_stride_elems, o, (int64_t)heads * head_dim,
+                                        batch, heads, tokens, head_dim, scale, false, 1.0f,
+                                        static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_destroy(siglip_model* m) {
+  if (!m) return SIGLIP_OK;
+  (void)hipDeviceSynchronize();
+  delete m;
+  return SIGLIP_OK;
+}
+
+SIGLIP_API const char* siglip_status_string(int status) {
+  switch (status) {
+    case SIGLIP_OK: return "SIGLIP_OK";
+    case SIGLIP_E_INVALID_ARG: return "SIGLIP_E_INVALID_ARG";
+    case SIGLIP_E_BAD_BLOB: return "SIGLIP_E_BAD_BLOB";
+    case SIGLIP_E_UNSUPPORTED: return "SIGLIP_E_UNSUPPORTED";
+    case SIGLIP_E_OUT_OF_MEMORY: return "SIGLIP_E_OUT_OF_MEMORY";
+    case SIGLIP_E_HIP: return "SIGLIP_E_HIP";
+  }
+  return "SIGLIP_E_UNKNOWN";
+}
+
+SIGLIP_API const char* siglip_last_error(void) { return g_last_error.c_str(); }
+
+SIGLIP_API int siglip_model_info(const siglip_model* m, int32_t* width, int32_t* layers, int32_t* heads,
+                                 int32_t* head_dim, int32_t* mlp, int32_t* tokens, int32_t* patch_dim,
+                                 int32_t* max_batch, int32_t* gemm_precision) {
+  if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
+  if (width) *width = m->width;
+  if (layers) *layers = m->layers;
+  if (heads) *heads = m->heads;
+  if (head_dim) *head_dim = m->head_dim;
+  if (mlp) *mlp = m->mlp;
+  if (tokens) *tokens = m->tokens;
+  if (patch_dim) *patch_dim = m->patch_dim;
+  if (max_batch) *max_batch = m->max_batch;
+  if (gemm_precision) *gemm_precision = m->fp8 ? 1 : 0;
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_debug_capture(siglip_model* m, int32_t layer) {
+  if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
+  if (layer >= m->layers) return fail(SIGLIP_E_INVALID_ARG, "capture layer beyond the model's layers");
+  m->captured = false;
+  if (layer < 0) {
+    m->capture_layer = -1;
+    return SIGLIP_OK;
+  }
+  try {
+    for (int s = 0; s < SIGLIP_STAGE_COUNT; ++s) {
+      if (m->cap[s]) continue;
+      int64_t r, c, l;
+      int32_t b;
+      stage_shape(m, s, m->max_batch, &r, &c, &l, &b);
+      m->cap_bytes[s] = (size_t)(r * l * b);
+      m->cap[s] = m->dalloc(m->cap_bytes[s]);
+    }
+    // the probe query is computed at create time; snapshot it now
+    hip_check(hipMemcpy(m->cap[SIGLIP_STAGE_MAP_Q], m->map_q, (size_t)m->width * 2, hipMemcpyDeviceToDevice),
+              "capture map_q");
+  } catch (const HipFail& f) {
+    return fail(SIGLIP_E_OUT_OF_MEMORY, f.where + ": " + hipGetErrorString(f.err));
+  }
+  m->capture_layer = layer;
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_debug_stage_info(const siglip_model* m, int32_t stage, int64_t* rows, int64_t* cols,
+                                       int64_t* ld, int32_t* elem_bytes) {
+  if (!m || stage < 0 || stage >= SIGLIP_STAGE_COUNT) return fail(SIGLIP_E_INVALID_ARG, "bad model or stage");
+  stage_shape(m, stage, m->captured ? m->captured_batch : m->max_batch, rows, cols, ld, elem_bytes);
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage, void* dst, size_t dst_bytes) {
+  if (!m || !dst || stage < 0 || stage >= SIGLIP_STAGE_COUNT) return fail(SIGLIP_E_INVALID_ARG, "bad arguments");
+  if (!m->captured && stage != SIGLIP_STAGE_MAP_Q) return fail(SIGLIP_E_INVALID_ARG, "no capturing encode yet");
+  if (!m->cap[stage]) return fail(SIGLIP_E_INVALID_ARG, "capture is off");
+  int64_t r, c, l;
+  int32_t b;
+  stage_shape(m, stage, m->captured ? m->captured_batch : 1, &r, &c, &l, &b);
+  const size_t n = (size_t)(r * l * b);
+  if (dst_bytes < n) return fail(SIGLIP_E_INVALID_ARG, "dst too small: need " + std::to_string(n) + " bytes");
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(dst, m->cap[stage], n, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("stage copy: ") + hipGetErrorString(e));
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_debug_fill_workspace(siglip_model* m, uint16_t pattern) {
+  if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
+  hipError_t e = launch_fill_u16(m->ws, m->ws_bytes / 2, pattern, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("fill: ") + hipGetErrorString(e));
+  return SIGLIP_OK;
+}
+
+}  // extern "C"
