@@ -1,0 +1,224 @@
+"""Throughput of the SigLIP So400m/14 image encoder on one MI355X.
+
+Workload (the throughput configuration): 27 encoder layers + MAP head, 378 px
+(729 tokens), batch 64, e4m3 GEMM operands at scale 2^-4 with F32
+accumulation, F16 attention, layernorm and residuals; synthetic N(0,1) patch
+vectors and Gaussian-Xavier weights (seed 2). Inputs are resident in HBM
+before the timed region. One step = one siglip_encode call on the batch.
+
+The JSON line also carries the batch-1 latency of the same model, the
+per-kernel-class launch times measured with HIP events inside the timed
+region, the roofline of the dominant kernel and a CPU baseline (the float64
+oracle on a one-image sample on the host cores).
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X dense peaks
+    "f16_mfma_tflops": 2500.0,
+    "fp8_mfma_tflops": 5000.0,
+    "hbm_gbs": 8000.0,
+}
+
+
+def algorithmic_flops_per_image(d, layers):
+    """Unpadded multiply-add count x2 of one image's forward pass."""
+    T, W, F, P, H, D = d.tokens, d.width, d.mlp, d.patch_dim, d.heads, d.head_dim
+    embed = 2 * T * P * W
+    layer = 2 * T * W * 3 * W + 4 * H * T * T * D + 2 * T * W * W + 2 * 2 * T * W * F
+    map_head = 2 * T * W * 2 * W + 4 * H * T * D + 2 * W * W + 2 * 2 * W * F
+    return embed + layers * layer + map_head
+
+
+def kernel_flops(cls, d, batch):
+    """Algorithmic FLOPs of ONE launch of a GEMM/attention class."""
+    M, W, F, T, H, D = batch * d.tokens, d.width, d.mlp, d.tokens, d.heads, d.head_dim
+    return {
+        "EMBED": 2 * M * d.patch_dim * W,
+        "QKV": 2 * M * W * 3 * W,
+        "ATTENTION": 4 * batch * H * T * T * D,
+        "OUT_PROJ": 2 * M * W * W,
+        "MLP_UP": 2 * M * W * F,
+        "MLP_DOWN": 2 * M * F * W,
+        "MAP_KV": 2 * M * W * 2 * W,
+    }.get(cls)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "vision_transformer_so400m_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(kernel_class):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_digest:\s*(\w+)", text)
+    if not m or m.group(1) != source_digest():
+        return None
+    m = re.search(rf"^\|\s*{kernel_class}\s*\|\s*([\d.eE+]+)\s*\|", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def cpu_baseline(wt, pixels, heads):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    t0 = time.perf_counter()
+    O.encode(wt, pixels[:1], heads)
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 4), "unit": "images/sec", "cores": int(cores), "kind": "oracle",
+            "sample": "image 0 of the batch-64 input, 27 layers + MAP, float64 numpy oracle "
+                      f"(unquantized), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--b1-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 512 MiB device copy (HBM-counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the encoder on a single MI355X "
+              "(data-parallel sharding is described, not built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    import vision_transformer_so400m_amd as V
+
+    cfg = S.CONFIGS["c4_27layer_b64_fp8"]
+    d = S.SO400M.with_depth(cfg["layers"])
+    B = cfg["batch"]
+    wt = S.make_weights(d, cfg["seed"])
+    pixels = S.make_pixels(d, B, cfg["seed"])
+    model = V.Model(S.pack_blob(d, wt), max_batch=B, fp8=cfg["fp8"])
+    x = torch.from_numpy(pixels).cuda()
+    out = torch.empty((B, 1, d.width), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        model.encode(x, out=out)
+    torch.cuda.synchronize()
+    ref_bits = out.clone()
+
+    # ---- timed region: exactly `steps` calls, synchronised on both sides
+    model.debug_timing(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        model.encode(x, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_class = {k: model.debug_timing_read(k) for k in V.KERNEL_CLASSES}
+    model.debug_timing(False)
+    ms_per_step = wall * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    deterministic = bool(torch.equal(out.view(torch.int16), ref_bits.view(torch.int16)))
+
+    flops_img = algorithmic_flops_per_image(d, d.depth)
+    value = B / (ms_per_step / 1e3)
+    tflops = flops_img * B / (ms_per_step / 1e3) / 1e12
+
+    kernels = {k: {"avg_us": round(ms * 1e3 / n, 2), "launches_per_step": n // args.steps,
+                   "share": round(ms / max(1e-9, sum(v[0] for v in per_class.values())), 4)}
+               for k, (ms, n) in per_class.items() if n}
+    dom = max(per_class, key=lambda k: per_class[k][0] if kernel_flops(k, d, B) else -1)
+    ms_dom, n_dom = per_class[dom]
+    avg_s = ms_dom / n_dom / 1e3
+    fl = kernel_flops(dom, d, B)
+    peak = PEAK["fp8_mfma_tflops"] if (cfg["fp8"] and dom != "ATTENTION") else PEAK["f16_mfma_tflops"]
+    achieved = fl / avg_s / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": profiled_traffic(dom),
+                "flops_per_launch": fl, "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    # ---- batch 1 latency on the same resident model
+    x1 = x[:1].contiguous()
+    o1 = torch.empty((1, 1, d.width), dtype=torch.float16, device="cuda")
+    for _ in range(5):
+        model.encode(x1, out=o1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.b1_steps):
+        model.encode(x1, out=o1)
+    torch.cuda.synchronize()
+    b1_ms = (time.perf_counter() - t0) * 1e3 / args.b1_steps
+
+    line = {
+        "metric": "images/sec, SigLIP So400m/14 378px 27-layer at B=1 and B=64; % MFMA peak",
+        "value": round(value, 2),
+        "unit": "images/sec",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 GEMM operands (f32 accumulate), f16 attention/layernorm/residuals",
+        "data": "synthetic (seeded N(0,1) patch vectors, Gaussian-Xavier weights, seed 2)",
+        "config": {"workload": "SigLIP So400m/14 378px image encoder, 27 layers + MAP head, batch 64, "
+                               "e4m3 GEMM operands at scale 2^-4",
+                   "batch": B, "layers": d.depth, "tokens": d.tokens, "width": d.width, "heads": d.heads,
+                   "head_dim": d.head_dim, "mlp": d.mlp, "parallelism": "single GPU"},
+        "tflops_algorithmic": round(tflops, 2),
+        "pct_f16_mfma_peak": round(100 * tflops / PEAK["f16_mfma_tflops"], 2),
+        "pct_fp8_mfma_peak": round(100 * tflops / PEAK["fp8_mfma_tflops"], 2),
+        "event_ms_per_step": round(ev_ms, 4),
+        "deterministic_across_steps": deterministic,
+        "b1": {"ms": round(b1_ms, 4), "images_per_s": round(1e3 / b1_ms, 2),
+               "workload": "same model and weights, batch 1"},
+        "kernels": kernels,
+        "roofline": roofline,
+        "context": {"ipu_27layer_b1_images_per_s": 110.4, "ipu_27layer_b2_images_per_s": 126.1,
+                    "note": "Graphcore IPU figures from the pages (FP8 projections), another machine"},
+    }
+    model.close()
+    del x, out
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wt, pixels, d.heads)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

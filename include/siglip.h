@@ -202,6 +202,34 @@ SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage,
  * transfers": padding is read, so unwritten tails must not be). Synchronous. */
 SIGLIP_API int siglip_debug_fill_workspace(siglip_model* m, uint16_t pattern);
 
+/* Kernel classes of one siglip_encode call, for per-launch timing. */
+typedef enum {
+  SIGLIP_K_INPUT = 0,       /* patch rows -> padded GEMM operand          */
+  SIGLIP_K_EMBED = 1,       /* patch GEMM + bias + positional embedding   */
+  SIGLIP_K_LAYERNORM = 2,   /* every encoder, final and MAP layernorm     */
+  SIGLIP_K_QKV = 3,         /* fused QKV GEMM + bias                      */
+  SIGLIP_K_ATTENTION = 4,   /* encoder flash attention                    */
+  SIGLIP_K_OUT_PROJ = 5,    /* output projection + bias + residual        */
+  SIGLIP_K_MLP_UP = 6,      /* MLP up GEMM + bias + GELU                  */
+  SIGLIP_K_MLP_DOWN = 7,    /* MLP down GEMM + bias + residual            */
+  SIGLIP_K_MAP_KV = 8,      /* MAP fused KV GEMM + bias                   */
+  SIGLIP_K_MAP_ATTENTION = 9, /* MAP probe attention                      */
+  SIGLIP_K_MAP_TAIL = 10,   /* MAP output projection and MLP GEMMs        */
+  SIGLIP_K_COUNT = 11
+} siglip_kernel_class;
+
+/* Turn per-launch timing on (enable != 0) or off for later siglip_encode
+ * calls on this model, and reset the totals. While on, every launch is
+ * bracketed by two HIP events recorded on the call's stream, so a launch's
+ * duration is the time between them on the GPU. Errors: INVALID_ARG. */
+SIGLIP_API int siglip_debug_timing(siglip_model* m, int32_t enable);
+
+/* Totals since timing was turned on for one kernel class: summed launch
+ * durations in milliseconds and the number of launches. Waits for the
+ * recorded events. Errors: INVALID_ARG, HIP. */
+SIGLIP_API int siglip_debug_timing_read(siglip_model* m, int32_t kernel_class,
+                                        double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

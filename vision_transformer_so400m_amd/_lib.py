@@ -29,7 +29,11 @@ STAGE = {n: i for i, n in enumerate(STAGES)}
 EXPORTED = ["siglip_create", "siglip_encode", "siglip_attention", "siglip_destroy",
             "siglip_status_string", "siglip_last_error", "siglip_model_info",
             "siglip_debug_capture", "siglip_debug_stage_info", "siglip_debug_stage",
-            "siglip_debug_fill_workspace"]
+            "siglip_debug_fill_workspace", "siglip_debug_timing", "siglip_debug_timing_read"]
+
+KERNEL_CLASSES = ["INPUT", "EMBED", "LAYERNORM", "QKV", "ATTENTION", "OUT_PROJ", "MLP_UP",
+                  "MLP_DOWN", "MAP_KV", "MAP_ATTENTION", "MAP_TAIL"]
+KCLASS = {n: i for i, n in enumerate(KERNEL_CLASSES)}
 
 
 class SiglipError(RuntimeError):
@@ -71,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.siglip_debug_stage_info.argtypes = [vp, i32, P(i64), P(i64), P(i64), P(i32)]
     lib.siglip_debug_stage.argtypes = [vp, i32, vp, ctypes.c_size_t]
     lib.siglip_debug_fill_workspace.argtypes = [vp, ctypes.c_uint16]
+    lib.siglip_debug_timing.argtypes = [vp, i32]
+    lib.siglip_debug_timing_read.argtypes = [vp, i32, P(ctypes.c_double), P(i64)]
     for name in EXPORTED:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
     _lib = lib
@@ -168,6 +174,17 @@ class Model:
 
     def debug_fill_workspace(self, pattern: int) -> None:
         _check(load_library().siglip_debug_fill_workspace(self.handle, pattern))
+
+    def debug_timing(self, enable: bool) -> None:
+        """Per-launch HIP-event timing of later encode calls (resets totals)."""
+        _check(load_library().siglip_debug_timing(self.handle, 1 if enable else 0))
+
+    def debug_timing_read(self, kclass) -> tuple:
+        """(total ms, launches) of one kernel class since timing was enabled."""
+        k = KCLASS[kclass] if isinstance(kclass, str) else kclass
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(load_library().siglip_debug_timing_read(self.handle, k, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:

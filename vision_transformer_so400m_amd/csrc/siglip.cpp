@@ -146,7 +146,17 @@ struct siglip_model {
   void* cap[SIGLIP_STAGE_COUNT] = {};
   size_t cap_bytes[SIGLIP_STAGE_COUNT] = {};
 
+  // per-launch timing: event pairs recorded around launches, resolved on read
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;        // 2 events per pending launch
+  std::vector<int> ev_class;              // class of each pending pair
+  size_t ev_used = 0;                     // pairs in use
+  bool timing_lost = false;               // an end event failed to record
+  double t_ms[SIGLIP_K_COUNT] = {};
+  int64_t t_n[SIGLIP_K_COUNT] = {};
+
   ~siglip_model() {
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
     for (void* p : allocs) (void)hipFree(p);
   }
 
@@ -239,6 +249,35 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
   if (eb) *eb = b;
 }
 
+// Brackets one launch with a pair of events when timing is on.
+class LaunchTimer {
+ public:
+  LaunchTimer(siglip_model* m, int kclass, hipStream_t s) : m_(m), s_(s) {
+    if (!m_->timing) return;
+    if (m_->ev_used * 2 + 2 > m_->ev_pool.size()) {
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t e;
+        hip_check(hipEventCreate(&e), "hipEventCreate");
+        m_->ev_pool.push_back(e);
+      }
+      m_->ev_class.push_back(kclass);
+    }
+    pair_ = m_->ev_used++;
+    m_->ev_class[pair_] = kclass;
+    hip_check(hipEventRecord(m_->ev_pool[2 * pair_], s_), "hipEventRecord");
+  }
+  ~LaunchTimer() {
+    // never throws: a failed record only loses this sample (the launch
+    // itself reports its own error)
+    if (m_->timing && hipEventRecord(m_->ev_pool[2 * pair_ + 1], s_) != hipSuccess) m_->timing_lost = true;
+  }
+
+ private:
+  siglip_model* m_;
+  hipStream_t s_;
+  size_t pair_ = 0;
+};
+
 void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) {
   const int M = B * m->tokens;
   const int W = m->width;
@@ -252,49 +291,97 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     return (size_t)(r * l * b);
   };
 
-  hip_check(launch_pad_convert(x, m->patch_dim, m->xp, M, m->patch_dim, m->patch_pad, q8, q8 ? m->op_scale : 1.0f, s),
-            "pad_convert");
-  gemm(m, m->embed, m->xp, m->patch_pad, M, m->h, W, EPI_BIAS_POS, false, nullptr, 0, s);
+  {
+    LaunchTimer lt(m, SIGLIP_K_INPUT, s);
+    hip_check(launch_pad_convert(x, m->patch_dim, m->xp, M, m->patch_dim, m->patch_pad, q8, q8 ? m->op_scale : 1.0f, s),
+              "pad_convert");
+  }
+  {
+    LaunchTimer lt(m, SIGLIP_K_EMBED, s);
+    gemm(m, m->embed, m->xp, m->patch_pad, M, m->h, W, EPI_BIAS_POS, false, nullptr, 0, s);
+  }
   if (cap) capture(m, SIGLIP_STAGE_EMBED, m->h, cb(SIGLIP_STAGE_EMBED), s);
 
   const float attn_scale = 1.0f / std::sqrt((float)m->head_dim);
   for (int i = 0; i < m->layers; ++i) {
     const Layer& Ly = m->L[i];
     const bool ci = cap && i == m->capture_layer;
-    hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
+    {
+      LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
+      hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
+    }
     if (ci) capture(m, SIGLIP_STAGE_LN1, m->a, cb(SIGLIP_STAGE_LN1), s);
-    gemm(m, Ly.qkv, m->a, W, M, m->qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    {
+      LaunchTimer lt(m, SIGLIP_K_QKV, s);
+      gemm(m, Ly.qkv, m->a, W, M, m->qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    }
     if (ci) capture(m, SIGLIP_STAGE_QKV, m->qkv, cb(SIGLIP_STAGE_QKV), s);
-    hip_check(launch_flash_attention(m->qkv, m->qkv + W, m->qkv + 2 * W, 3 * W, m->o, W, B, m->heads, m->tokens,
-                                     m->head_dim, attn_scale, q8, m->op_scale, s),
-              "attention");
+    {
+      LaunchTimer lt(m, SIGLIP_K_ATTENTION, s);
+      hip_check(launch_flash_attention(m->qkv, m->qkv + W, m->qkv + 2 * W, 3 * W, m->o, W, B, m->heads, m->tokens,
+                                       m->head_dim, attn_scale, q8, m->op_scale, s),
+                "attention");
+    }
     if (ci) capture(m, SIGLIP_STAGE_ATTN, m->o, cb(SIGLIP_STAGE_ATTN), s);
-    gemm(m, Ly.out, m->o, W, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+    {
+      LaunchTimer lt(m, SIGLIP_K_OUT_PROJ, s);
+      gemm(m, Ly.out, m->o, W, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+    }
     if (ci) capture(m, SIGLIP_STAGE_H_ATTN, m->h, cb(SIGLIP_STAGE_H_ATTN), s);
-    hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
+    {
+      LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
+      hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
+    }
     if (ci) capture(m, SIGLIP_STAGE_LN2, m->a, cb(SIGLIP_STAGE_LN2), s);
-    gemm(m, Ly.mlp1, m->a, W, M, m->u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+    {
+      LaunchTimer lt(m, SIGLIP_K_MLP_UP, s);
+      gemm(m, Ly.mlp1, m->a, W, M, m->u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+    }
     if (ci) capture(m, SIGLIP_STAGE_MLP_HIDDEN, m->u, cb(SIGLIP_STAGE_MLP_HIDDEN), s);
-    gemm(m, Ly.mlp2, m->u, m->mlp_pad, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+    {
+      LaunchTimer lt(m, SIGLIP_K_MLP_DOWN, s);
+      gemm(m, Ly.mlp2, m->u, m->mlp_pad, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+    }
     if (ci) capture(m, SIGLIP_STAGE_H_OUT, m->h, cb(SIGLIP_STAGE_H_OUT), s);
   }
 
-  hip_check(launch_layernorm(m->h, W, m->a, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, q8, m->op_scale, s), "final ln");
+  {
+    LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
+    hip_check(launch_layernorm(m->h, W, m->a, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, q8, m->op_scale, s), "final ln");
+  }
   if (cap) capture(m, SIGLIP_STAGE_FINAL_LN, m->a, cb(SIGLIP_STAGE_FINAL_LN), s);
   f16* kv = m->qkv;  // [M, 2W]
-  gemm(m, m->mkv, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+  {
+    LaunchTimer lt(m, SIGLIP_K_MAP_KV, s);
+    gemm(m, m->mkv, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+  }
   if (cap) capture(m, SIGLIP_STAGE_MAP_KV, kv, cb(SIGLIP_STAGE_MAP_KV), s);
-  hip_check(launch_map_attention(m->map_q, kv, 2 * W, W, m->mo, W, B, m->heads, m->tokens, m->head_dim, attn_scale,
-                                 q8, m->op_scale, s),
-            "map attention");
+  {
+    LaunchTimer lt(m, SIGLIP_K_MAP_ATTENTION, s);
+    hip_check(launch_map_attention(m->map_q, kv, 2 * W, W, m->mo, W, B, m->heads, m->tokens, m->head_dim, attn_scale,
+                                   q8, m->op_scale, s),
+              "map attention");
+  }
   if (cap) capture(m, SIGLIP_STAGE_MAP_ATTN, m->mo, cb(SIGLIP_STAGE_MAP_ATTN), s);
-  gemm(m, m->mout, m->mo, W, B, m->my, W, EPI_BIAS, false, nullptr, 0, s);
+  {
+    LaunchTimer lt(m, SIGLIP_K_MAP_TAIL, s);
+    gemm(m, m->mout, m->mo, W, B, m->my, W, EPI_BIAS, false, nullptr, 0, s);
+  }
   if (cap) capture(m, SIGLIP_STAGE_MAP_Y, m->my, cb(SIGLIP_STAGE_MAP_Y), s);
-  hip_check(launch_layernorm(m->my, W, m->ma, W, m->mln_g, m->mln_b, B, W, 1e-6f, q8, m->op_scale, s), "map ln");
+  {
+    LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
+    hip_check(launch_layernorm(m->my, W, m->ma, W, m->mln_g, m->mln_b, B, W, 1e-6f, q8, m->op_scale, s), "map ln");
+  }
   if (cap) capture(m, SIGLIP_STAGE_MAP_LN, m->ma, cb(SIGLIP_STAGE_MAP_LN), s);
-  gemm(m, m->mmlp1, m->ma, W, B, m->mu, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+  {
+    LaunchTimer lt(m, SIGLIP_K_MAP_TAIL, s);
+    gemm(m, m->mmlp1, m->ma, W, B, m->mu, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+  }
   if (cap) capture(m, SIGLIP_STAGE_MAP_HIDDEN, m->mu, cb(SIGLIP_STAGE_MAP_HIDDEN), s);
-  gemm(m, m->mmlp2, m->mu, m->mlp_pad, B, out, W, EPI_BIAS_RES, false, m->my, W, s);
+  {
+    LaunchTimer lt(m, SIGLIP_K_MAP_TAIL, s);
+    gemm(m, m->mmlp2, m->mu, m->mlp_pad, B, out, W, EPI_BIAS_RES, false, m->my, W, s);
+  }
   if (cap) {
     m->captured = true;
     m->captured_batch = B;
@@ -633,6 +720,36 @@ SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage, void* ds
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(dst, m->cap[stage], n, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("stage copy: ") + hipGetErrorString(e));
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_debug_timing(siglip_model* m, int32_t enable) {
+  if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
+  m->timing = enable != 0;
+  m->ev_used = 0;
+  m->timing_lost = false;
+  for (int k = 0; k < SIGLIP_K_COUNT; ++k) {
+    m->t_ms[k] = 0.0;
+    m->t_n[k] = 0;
+  }
+  return SIGLIP_OK;
+}
+
+SIGLIP_API int siglip_debug_timing_read(siglip_model* m, int32_t kernel_class, double* total_ms, int64_t* launches) {
+  if (!m || kernel_class < 0 || kernel_class >= SIGLIP_K_COUNT) return fail(SIGLIP_E_INVALID_ARG, "bad model or class");
+  // fold every pending pair into the totals, then recycle the events
+  for (size_t i = 0; i < m->ev_used; ++i) {
+    hipError_t e = hipEventSynchronize(m->ev_pool[2 * i + 1]);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, m->ev_pool[2 * i], m->ev_pool[2 * i + 1]);
+    if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("timing read: ") + hipGetErrorString(e));
+    m->t_ms[m->ev_class[i]] += ms;
+    m->t_n[m->ev_class[i]] += 1;
+  }
+  m->ev_used = 0;
+  if (m->timing_lost) return fail(SIGLIP_E_HIP, "an end-of-launch event failed to record");
+  if (total_ms) *total_ms = m->t_ms[kernel_class];
+  if (launches) *launches = m->t_n[kernel_class];
   return SIGLIP_OK;
 }
 
