@@ -43,22 +43,35 @@ constexpr int VROWS = 96; // padded head width of the PV output (3 x 32)
 constexpr int VST = 68;   // V^T tile row stride in halfs (136 B)
 constexpr float kNegInf = -__builtin_inff();
 
+// Linear workgroup id -> logical block, XCD-aware: workgroups are dispatched
+// round-robin over the 8 XCDs; the remap gives each XCD a contiguous range of
+// logical blocks, so the query blocks of one (image, head) share an L2 and
+// read that head's K and V from HBM once.
+__device__ __forceinline__ int xcd_block(int id, int total) {
+  const int total8 = total & ~7;
+  return id < total8 ? (id & 7) * (total8 >> 3) + (id >> 3) : id;
+}
+
 template <bool OUT_FP8>
-__global__ __launch_bounds__(256) void flash_attn_kernel(
+__global__ __launch_bounds__(256, 2) void flash_attn_kernel(
     const f16* __restrict__ q, const f16* __restrict__ k, const f16* __restrict__ v, int64_t ld,
-    void* __restrict__ o, int64_t ldo, int T, int D, float sl2, float out_scale) {
-  __shared__ __attribute__((aligned(16))) f16 Ks[KB * KST];
-  __shared__ __attribute__((aligned(16))) f16 Vt[VROWS * VST];
+    void* __restrict__ o, int64_t ldo, int T, int D, int H, int nqb, float c, float out_scale) {
+  __shared__ __attribute__((aligned(16))) f16 Ks[2][KB * KST];
+  __shared__ __attribute__((aligned(16))) f16 Vt[2][VROWS * VST];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
   const int fr = lane & 31;
   const int fg = lane >> 5;
-  const int b = blockIdx.z;
-  const int hc = blockIdx.y * D;
+  const int L = xcd_block(blockIdx.x, gridDim.x);
+  const int qb = L % nqb;
+  const int bh = L / nqb;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int hc = h * D;
   const int64_t img = (int64_t)b * T;
-  const int qi = blockIdx.x * QB + wave * 32 + fr;  // this lane's query
+  const int qi = qb * QB + wave * 32 + fr;  // this lane's query
 
   // Q fragments: query qi, head dims 16s + 8fg .. +7 (zero past D and T)
   f16x8 qf[5];
@@ -70,8 +83,60 @@ __global__ __launch_bounds__(256) void flash_attn_kernel(
     else
       qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  // V^T rows D..95 stay zero for the whole kernel
-  for (int i = t; i < (VROWS - D) * VST; i += 256) Vt[D * VST + i] = (f16)0.0f;
+  // V^T rows D..95 stay zero for the whole kernel (both buffers)
+  for (int i = t; i < 2 * (VROWS - D) * VST; i += 256) {
+    const int bsel = i / ((VROWS - D) * VST), r = i % ((VROWS - D) * VST);
+    Vt[bsel][D * VST + r] = (f16)0.0f;
+  }
+
+  // ---- staging of one 64-key block into registers, then into LDS.
+  // K: 64 keys x 10 chunks of 8 dims (zero past D), 3 chunks per thread.
+  // V: thread t < 8*nvc owns 8 consecutive keys x one 8-dim chunk and writes
+  //    it transposed (8 rows of V^T, 8 keys each).
+  const int nvc = D >> 3;
+  const bool vown = t < 8 * nvc;
+  const int vkg = t / max(nvc, 1), vc = t % max(nvc, 1);
+  i32x4 kr[3];
+  f16x8 vr[8];
+  auto gload = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int cidx = t + 256 * i;
+      const int key = cidx / 10, ch = cidx % 10;
+      const int kk = key0 + key;
+      kr[i] = i32x4{0, 0, 0, 0};
+      if (cidx < KB * 10 && kk < T && ch * 8 < D)
+        kr[i] = *reinterpret_cast<const i32x4*>(k + (img + kk) * ld + hc + ch * 8);
+    }
+    if (vown) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = key0 + 8 * vkg + j;
+        vr[j] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (kk < T) vr[j] = *reinterpret_cast<const f16x8*>(v + (img + kk) * ld + hc + 8 * vc);
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int cidx = t + 256 * i;
+      if (cidx < KB * 10) {
+        const int key = cidx / 10, ch = cidx % 10;
+        *reinterpret_cast<i32x4*>(&Ks[buf][key * KST + ch * 8]) = kr[i];
+      }
+    }
+    if (vown) {
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const f16x4 lo = {vr[0][dd], vr[1][dd], vr[2][dd], vr[3][dd]};
+        const f16x4 hi = {vr[4][dd], vr[5][dd], vr[6][dd], vr[7][dd]};
+        f16* row = &Vt[buf][(8 * vc + dd) * VST + 8 * vkg];
+        *reinterpret_cast<f16x4*>(row) = lo;
+        *reinterpret_cast<f16x4*>(row + 4) = hi;
+      }
+    }
+  };
 
   float m_run = kNegInf, l_run = 0.0f;
   f32x16 oacc[3];
@@ -81,28 +146,15 @@ __global__ __launch_bounds__(256) void flash_attn_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
 
   const int nkb = (T + KB - 1) / KB;
-  const int vch = D >> 3;
+  gload(0);
+  sstore(0);
+  __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
     const int key0 = kb * KB;
-    __syncthreads();  // every wave is done reading the previous block
-    for (int c = t; c < KB * 10; c += 256) {
-      const int key = c / 10, ch = c % 10;
-      const int kk = key0 + key;
-      i32x4 val = {0, 0, 0, 0};
-      if (kk < T && ch * 8 < D) val = *reinterpret_cast<const i32x4*>(k + (img + kk) * ld + hc + ch * 8);
-      *reinterpret_cast<i32x4*>(&Ks[key * KST + ch * 8]) = val;
-    }
-    for (int c = t; c < KB * vch; c += 256) {
-      const int key = c / vch, ch = c % vch;
-      const int kk = key0 + key;
-      f16x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (kk < T) val = *reinterpret_cast<const f16x8*>(v + (img + kk) * ld + hc + ch * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Vt[(ch * 8 + i) * VST + key] = val[i];
-    }
-    __syncthreads();
+    if (kb + 1 < nkb) gload(key0 + KB);  // next block in flight during this one
 
-    // S^T[key][query] for keys key0 + 32kt + (8(r/4) + 4fg + r%4)
+    // S^T[key][query] (raw dot products) for keys key0 + 32kt + (8(r/4) + 4fg + r%4)
     f32x16 sacc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -110,39 +162,45 @@ __global__ __launch_bounds__(256) void flash_attn_kernel(
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(&Ks[(32 * kt + fr) * KST + 16 * s + 8 * fg]);
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(&Ks[buf][(32 * kt + fr) * KST + 16 * s + 8 * fg]);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
       }
+    }
+    if (key0 + KB > T) {  // only the last block holds keys past T
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3) >= T) sacc[kt][r] = kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3);
-        const float sv = key < T ? sacc[kt][r] * sl2 : kNegInf;
-        sacc[kt][r] = sv;
-        mx = fmaxf(mx, sv);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float mc = m_new * c;
     float ls = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], c, -mc));  // exp(scale (s - m))
         sacc[kt][r] = p;
         ls += p;
       }
     ls += __shfl_xor(ls, 32, 64);
-    l_run = l_run * alpha + ls;
+    if (!__all(m_new == m_run)) {  // some row's maximum moved: rescale the state
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    l_run += ls;
     m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 3; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
 
     // O^T[d][query] += V^T[d][keys] P^T[keys][query], 16 keys per step; the
     // lane group fg slots hold keys 16s + 4fg + (0..3) then 16s + 8 + 4fg + (0..3)
@@ -154,13 +212,15 @@ __global__ __launch_bounds__(256) void flash_attn_kernel(
       for (int e = 0; e < 8; ++e) pf[e] = (f16)sacc[kt][base + e];
 #pragma unroll
       for (int dt = 0; dt < 3; ++dt) {
-        const f16* vr = &Vt[(32 * dt + fr) * VST + 16 * s + 4 * fg];
-        const f16x4 lo = *reinterpret_cast<const f16x4*>(vr);
-        const f16x4 hi = *reinterpret_cast<const f16x4*>(vr + 8);
+        const f16* vrow = &Vt[buf][(32 * dt + fr) * VST + 16 * s + 4 * fg];
+        const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow);
+        const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + 8);
         const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[dt], 0, 0, 0);
       }
     }
+    if (kb + 1 < nkb) sstore(buf ^ 1);  // the other buffer was last read in block kb-1
+    __syncthreads();
   }
 
   if (qi >= T) return;
@@ -276,11 +336,16 @@ hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v, int6
     return hipErrorInvalidValue;
   if (batch > 65535 || heads > 65535) return hipErrorInvalidValue;
   const float sl2 = scale * 1.4426950408889634f;
-  dim3 grid((tokens + QB - 1) / QB, heads, batch);
+  const int nqb = (tokens + QB - 1) / QB;
+  const int64_t blocks = (int64_t)nqb * heads * batch;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
   if (out_fp8)
-    hipLaunchKernelGGL(flash_attn_kernel<true>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, sl2, out_scale);
+    hipLaunchKernelGGL(flash_attn_kernel<true>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, heads,
+                       nqb, sl2, out_scale);
   else
-    hipLaunchKernelGGL(flash_attn_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, sl2, out_scale);
+    hipLaunchKernelGGL(flash_attn_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, heads,
+                       nqb, sl2, out_scale);
   return hipGetLastError();
 }
 

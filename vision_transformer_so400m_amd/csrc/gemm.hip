@@ -14,7 +14,7 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales; the power-of-two
 // operand scale is folded into acc_scale). F32 accumulation.
 //
-// Tiling: a workgroup of 4 waves owns a BM x BN output tile and walks K in
+// Tiling: a workgroup of 4 or 8 waves owns a BM x BN output tile and walks K in
 // 128-byte slices (64 F16 or 128 e4m3 values per row). Slices are staged
 // global -> registers -> LDS, double-buffered so the loads of slice k+1 are in
 // flight while slice k is multiplied. LDS rows are 128 bytes with the 16-byte
@@ -36,20 +36,49 @@ template <int BM, int BN, int WM, int WN>
 struct Tile {
   static constexpr int WAVES_N = BN / WN;
   static constexpr int WAVES_M = BM / WM;
-  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int TM = WM / 32;
   static constexpr int TN = WN / 32;
-  static constexpr int A_LOADS = BM / 32;  // 16-byte global loads per thread
-  static constexpr int W_LOADS = BN / 32;
+  static constexpr int ROWS_PER_ROUND = 8 * WAVES;  // tile rows one DMA round fills
+  static_assert(BM % ROWS_PER_ROUND == 0 && BN % ROWS_PER_ROUND == 0, "whole DMA rounds");
   static constexpr int STAGE = (BM + BN) * kRowBytes;
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-template <int BM, int BN, int WM, int WN, bool FP8, int EPI, bool OUT_FP8>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+// Linear workgroup id -> output tile. Workgroups are dispatched round-robin
+// over the 8 XCDs (id % 8), each with its own L2. The remap gives every XCD
+// a contiguous range of tiles, and tiles are numbered N-fastest, so the
+// workgroups that share one row block of A run on the same XCD at about the
+// same time and read that block from HBM once.
+__device__ __forceinline__ void tile_of(int id, int total, int ntn, int* tm, int* tn) {
+  const int total8 = total & ~7;
+  const int L = id < total8 ? (id & 7) * (total8 >> 3) + (id >> 3) : id;
+  *tm = L / ntn;
+  *tn = L - *tm * ntn;
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): the
+// wave writes 64 x 16 bytes contiguously from lds_wave_base, lane i at +16 i.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmArgs g) {
   using T = Tile<BM, BN, WM, WN>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+  static_assert(STAGES >= 2, "at least double buffering");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * T::STAGE];
 
   constexpr int E = FP8 ? 1 : 2;
   const int t = threadIdx.x;
@@ -57,46 +86,38 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int wave = t >> 6;
   const int wm = wave / T::WAVES_N;
   const int wn = wave % T::WAVES_N;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int ntn = g.N / BN;
+  const int ntm = (g.M + BM - 1) / BM;
+  int tm, tn;
+  tile_of(blockIdx.x, ntm * ntn, ntn, &tm, &tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
   const int nk = (g.K * E) / kRowBytes;
 
-  // ---- global -> register staging assignment: 8 threads per 128-byte row
-  const int lr = t >> 3;
-  const int lc = t & 7;
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(g.a) + lc * 16;
-  const uint8_t* wbase = reinterpret_cast<const uint8_t*>(g.w) + lc * 16;
-  uint32_t aoff[T::A_LOADS];
-  uint32_t woff[T::W_LOADS];
+  // ---- global -> LDS transfer assignment. A stage holds BM rows of A then
+  // BN rows of Wt, 128 bytes each, chunk-swizzled. Transfer j of wave w
+  // fills tile rows R j + 8 w .. +7 (R = 8 x waves); lane i lands at row
+  // R j + 8 w + i/8, physical chunk i%8, so it fetches logical chunk
+  // (i%8) ^ (i/8).
+  constexpr int R = T::ROWS_PER_ROUND;
+  constexpr int CH = (BM + BN) / R;  // transfers per thread per stage
+  const int rr = lane >> 3;
+  const int lchunk = (lane & 7) ^ rr;
+  const uint8_t* src[CH];
 #pragma unroll
-  for (int i = 0; i < T::A_LOADS; ++i) {
-    int row = min(m0 + lr + 32 * i, g.M - 1);  // rows past M re-read row M-1; never stored
-    aoff[i] = (uint32_t)((int64_t)row * g.lda * E);
+  for (int j = 0; j < CH; ++j) {
+    const int row = R * j + 8 * wave + rr;
+    if (R * j < BM) {
+      const int am = min(m0 + row, g.M - 1);  // rows past M re-read row M-1; never stored
+      src[j] = reinterpret_cast<const uint8_t*>(g.a) + (int64_t)am * g.lda * E + lchunk * 16;
+    } else {
+      src[j] = reinterpret_cast<const uint8_t*>(g.w) + (int64_t)(n0 + row - BM) * g.ldw * E + lchunk * 16;
+    }
   }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % STAGES) * T::STAGE + 8 * wave * kRowBytes;
 #pragma unroll
-  for (int i = 0; i < T::W_LOADS; ++i)
-    woff[i] = (uint32_t)((int64_t)(n0 + lr + 32 * i) * g.ldw * E);
-  const int lds_st = lr * kRowBytes + swz(lr, lc) * 16;  // + 32*i rows keeps (row & 7)
-
-  i32x4 ra[T::A_LOADS], rw[T::W_LOADS];
-  auto gload = [&](int kt) {
-    const int kb = kt * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i)
-      ra[i] = *reinterpret_cast<const i32x4*>(abase + aoff[i] + kb);
-#pragma unroll
-    for (int i = 0; i < T::W_LOADS; ++i)
-      rw[i] = *reinterpret_cast<const i32x4*>(wbase + woff[i] + kb);
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* sa = smem + buf * T::STAGE;
-    uint8_t* sw = sa + BM * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i)
-      *reinterpret_cast<i32x4*>(sa + lds_st + 32 * i * kRowBytes) = ra[i];
-#pragma unroll
-    for (int i = 0; i < T::W_LOADS; ++i)
-      *reinterpret_cast<i32x4*>(sw + lds_st + 32 * i * kRowBytes) = rw[i];
+    for (int j = 0; j < CH; ++j) dma16(src[j] + kt * kRowBytes, st + R * j * kRowBytes);
   };
 
   f32x16 acc[T::TM][T::TN];
@@ -163,15 +184,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  // prologue: the first STAGES-1 slices in flight
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nk) issue(p);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    compute(cur);
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    // this thread's transfers of slice kt are done when at most the newer
+    // slices' transfers remain; the barrier then makes every wave's visible
+    // and guarantees that slice kt-1's buffer is no longer being read
+    if (kt + STAGES - 2 < nk)
+      wait_vmcnt<(STAGES - 2) * CH>();
+    else
+      wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    compute(kt % STAGES);
   }
 
   // ---- epilogue: lane holds row m = tile row + fr, columns 8q + 4fg + (0..3)
@@ -215,20 +242,29 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool FP8, int EPI, bool OUT_FP8>
+template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
-  dim3 grid(g.N / BN, (g.M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, FP8, EPI, OUT_FP8>), grid, dim3(256), 0, s, g);
+  if (g.N % BN != 0) return hipErrorInvalidValue;  // every column tile must be whole
+  dim3 grid((g.N / BN) * ((g.M + BM - 1) / BM));
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, FP8, EPI, OUT_FP8>), grid,
+                     dim3(Tile<BM, BN, WM, WN>::THREADS), 0, s, g);
   return hipGetLastError();
 }
 
 template <bool FP8, int EPI, bool OUT_FP8>
 hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
-  const long tiles_l = (long)((g.M + 255) / 256) * (g.N / 128);
-  const long tiles_m = (long)((g.M + 127) / 128) * (g.N / 128);
-  if (tiles_l >= 1024) return launch_cfg<256, 128, 128, 64, FP8, EPI, OUT_FP8>(g, s);
-  if (tiles_m >= 512) return launch_cfg<128, 128, 64, 64, FP8, EPI, OUT_FP8>(g, s);
-  return launch_cfg<64, 64, 32, 32, FP8, EPI, OUT_FP8>(g, s);
+  // Tile choice measured on the batch-64 shapes (M = 46,656): eight-wave
+  // 256-row tiles (two waves per SIMD, 128x64 or 64x64 per wave) for wide N,
+  // four-wave 128x128 tiles with two LDS stages (two workgroups per CU) for
+  // N = 1152; small M falls back to tiles that still fill the 256 CUs.
+  const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
+  if (tiles_128 >= 1024) {
+    if (g.N % 256 == 0) return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(g, s);
+    if (g.N >= 2048) return launch_cfg<256, 128, 64, 64, FP8 ? 2 : 3, FP8, EPI, OUT_FP8>(g, s);
+    return launch_cfg<128, 128, 64, 64, 2, FP8, EPI, OUT_FP8>(g, s);
+  }
+  if (tiles_128 >= 384) return launch_cfg<128, 128, 64, 64, 2, FP8, EPI, OUT_FP8>(g, s);
+  return launch_cfg<64, 64, 32, 32, 3, FP8, EPI, OUT_FP8>(g, s);
 }
 
 template <bool FP8>
