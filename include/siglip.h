@@ -173,7 +173,11 @@ typedef enum {
   SIGLIP_STAGE_MAP_LN = 12,    /* [B, width]   F16 | e4m3 code                */
   SIGLIP_STAGE_MAP_HIDDEN = 13,/* [B, mlp_pad] F16 | e4m3 code (post-GELU)    */
   SIGLIP_STAGE_MAP_Q = 14,     /* [1, width]   F16  probe query (create time) */
-  SIGLIP_STAGE_COUNT = 15
+  SIGLIP_STAGE_V_T = 15,       /* [B*heads*head_dim, round_up(tokens,64)] F16:
+                                  V of each (image, head) transposed (dims x
+                                  tokens, zeros past tokens); when present, the
+                                  QKV stage holds only the Q and K columns     */
+  SIGLIP_STAGE_COUNT = 16
 } siglip_stage;
 
 /* Capture stage outputs on later siglip_encode calls: layer-local stages

@@ -229,10 +229,11 @@ def check_stages(model, wt, x, dims, fp8, batch):
     st = {n: _stage(model, n) for n in
           ["EMBED", "LN1", "QKV", "ATTN", "H_ATTN", "LN2", "MLP_HIDDEN", "H_OUT", "FINAL_LN",
            "MAP_KV", "MAP_ATTN", "MAP_Y", "MAP_LN", "MAP_HIDDEN", "MAP_Q"]}
+
     dw = lambda n: device_weight(wt, n, fp8, se)
     f = lambda n: _dec(model, st[n], fp8)
 
-    def gemm_check(name, xin, wname, bname, add=None, gelu=False):
+    def gemm_check(name, xin, wname, bname, add=None, gelu=False, cols=None):
         w = dw(wname)
         ref = O.linear(xin, w, wt[bname].astype(np.float64))
         extra = acc_tol(xin, w)
@@ -241,10 +242,14 @@ def check_stages(model, wt, x, dims, fp8, batch):
         if gelu:
             ref = O.gelu_tanh(ref)
             extra = extra * 1.2
-        if fp8 and st[name].dtype == np.uint8:
-            e4m3_neighbours_ok(name, st[name], ref, se, band=extra)
+        gpu = st[name]
+        if cols is not None:   # the stage holds only the leading columns
+            ref, extra = ref[:, :cols], extra[:, :cols]
+        if fp8 and gpu.dtype == np.uint8:
+            e4m3_neighbours_ok(name, gpu, ref, se, band=extra)
         else:
-            assert_close(name, st[name], ref, extra=extra + 1e-6)
+            assert_close(name, gpu, ref, extra=extra + 1e-6)
+        return ref, extra
 
     def ln_check(name, hin, p):
         ref = O.layer_norm(hin, wt[p + ".g"].astype(np.float64), wt[p + ".b"].astype(np.float64))
@@ -259,8 +264,21 @@ def check_stages(model, wt, x, dims, fp8, batch):
     pos = np.tile(wt["pos"].astype(np.float64), (batch, 1))
     gemm_check("EMBED", xin, "embed.w", "embed.b", add=pos)
     ln_check("LN1", f("EMBED"), "layer0.ln1")
-    gemm_check("QKV", f("LN1"), "layer0.qkv.w", "layer0.qkv.b")
-    qkv = f("QKV").reshape(batch, T, 3 * W)
+    qk_cols = st["QKV"].shape[1]
+    gemm_check("QKV", f("LN1"), "layer0.qkv.w", "layer0.qkv.b", cols=qk_cols)
+    if qk_cols == 2 * W:
+        # V arrives transposed per head: rows (b*H + h)*D + d, tokens padded with zeros
+        vt_full = model.debug_stage("V_T", full=True)
+        assert vt_full.shape[0] == batch * H * D and vt_full.shape[1] >= T and vt_full.shape[1] % 64 == 0
+        assert not vt_full[:, T:].view(np.uint16).any(), "V^T padding must be exact zeros"
+        v_gpu = vt_full[:, :T].reshape(batch, H, D, T).transpose(0, 3, 1, 2).reshape(M, W)
+        st["V_FROM_VT"] = v_gpu
+        w = dw("layer0.qkv.w")[:, 2 * W:]
+        ref_v = O.linear(f("LN1"), w, wt["layer0.qkv.b"][2 * W:].astype(np.float64))
+        assert_close("V (from V^T)", v_gpu, ref_v, extra=acc_tol(f("LN1"), w) + 1e-6)
+        qkv = np.concatenate([f("QKV"), v_gpu.astype(np.float64)], axis=1).reshape(batch, T, 3 * W)
+    else:
+        qkv = f("QKV").reshape(batch, T, 3 * W)
     ref_attn = _attn_ref(qkv[..., :W], qkv[..., W:2 * W], qkv[..., 2 * W:], H, D, 1 / math.sqrt(D)).reshape(M, W)
     attn_extra = _attn_extra(qkv[..., 2 * W:], H, D).reshape(M, W) + 1e-6
     if fp8:

@@ -23,7 +23,7 @@ SIGLIP_E_OUT_OF_MEMORY = -4
 SIGLIP_E_HIP = -5
 
 STAGES = ["EMBED", "LN1", "QKV", "ATTN", "H_ATTN", "LN2", "MLP_HIDDEN", "H_OUT",
-          "FINAL_LN", "MAP_KV", "MAP_ATTN", "MAP_Y", "MAP_LN", "MAP_HIDDEN", "MAP_Q"]
+          "FINAL_LN", "MAP_KV", "MAP_ATTN", "MAP_Y", "MAP_LN", "MAP_HIDDEN", "MAP_Q", "V_T"]
 STAGE = {n: i for i, n in enumerate(STAGES)}
 
 EXPORTED = ["siglip_create", "siglip_encode", "siglip_attention", "siglip_destroy",

@@ -43,6 +43,13 @@ constexpr int VROWS = 96; // padded head width of the PV output (3 x 32)
 constexpr int VST = 68;   // V^T tile row stride in halfs (136 B)
 constexpr float kNegInf = -__builtin_inff();
 
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): the
+// wave writes 64 x 16 bytes contiguously from lds_wave_base, lane i at +16 i.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 // Linear workgroup id -> logical block, XCD-aware: workgroups are dispatched
 // round-robin over the 8 XCDs; the remap gives each XCD a contiguous range of
 // logical blocks, so the query blocks of one (image, head) share an L2 and
@@ -243,6 +250,222 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Encoder attention with V already transposed per head (written that way by
+// the QKV GEMM epilogue). Both operands of a 64-key block then stream
+// global -> LDS with global_load_lds_dwordx4 into a 3-stage ring, exactly as
+// the GEMM operands do: no register staging and no transposition here.
+//
+// LDS stage (bytes): K [64 keys x 176] (11 chunks of 16 B per key: 9 chunks of
+// dims, then copies of the last dim chunk, which meet the zero Q padding), then
+// V^T [96 dims x 128] (64 keys per row, 16-byte chunk index XOR (dim & 7);
+// rows D..95 are zeros written once). Keys past T read token T-1 (finite,
+// masked to -inf); V^T columns past T are zeros in memory.
+constexpr int VK_PITCH = 176;
+constexpr int VK_BYTES = KB * VK_PITCH;          // 11 x 1 KiB
+constexpr int VV_PITCH = 128;
+constexpr int VT_STAGE = VK_BYTES + VROWS * VV_PITCH;
+constexpr int VT_STAGES = 3;
+
+template <int N>
+__device__ __forceinline__ void attn_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D, bool OUT_FP8>
+__global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
+    const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
+    int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
+  static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
+  constexpr int NDC = D / 8;                     // 16-byte dim chunks per key
+  constexpr int NDMA = VK_BYTES / 1024 + D / 8;  // 1 KiB transfers per stage
+  constexpr int PER_WAVE = (NDMA + 3) / 4;       // every wave issues the same count
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[VT_STAGES * VT_STAGE + 1024];
+  uint8_t* trash = smem + VT_STAGES * VT_STAGE;  // target of the padding transfers
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int fr = lane & 31;
+  const int fg = lane >> 5;
+  const int L = xcd_block(blockIdx.x, gridDim.x);
+  const int qb = L % nqb;
+  const int bh = L / nqb;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int hc = h * D;
+  const int64_t img = (int64_t)b * T;
+  const int qi = qb * QB + wave * 32 + fr;
+  const f16* vth = vt + (int64_t)bh * D * vt_ld;  // this head's V^T rows
+
+  f16x8 qf[5];
+#pragma unroll
+  for (int s = 0; s < 5; ++s) {
+    const int d0 = 16 * s + 8 * fg;
+    if (qi < T && d0 < D)
+      qf[s] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
+    else
+      qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  // zero V^T rows D..95 of every stage once
+  constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
+  for (int i = t; i < VT_STAGES * ZCH; i += 256) {
+    uint8_t* z = smem + (i / ZCH) * VT_STAGE + VK_BYTES + D * VV_PITCH + (i % ZCH) * 16;
+    *reinterpret_cast<i32x4*>(z) = i32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  // transfer slot j of this wave: global index jg = wave + 4 j
+  int krow[PER_WAVE], kdc[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int jg = wave + 4 * j;
+    const int off = jg * 1024 + 16 * lane;
+    krow[j] = off / VK_PITCH;
+    kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
+  }
+  const int vd_lo = lane >> 3;                 // V^T row within a transfer
+  const int vchunk = (lane & 7);               // physical chunk of this lane
+  auto issue = [&](int kb) {
+    const int key0 = kb * KB;
+    uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int jg = wave + 4 * j;
+      if (jg < VK_BYTES / 1024) {
+        const int key = min(key0 + krow[j], T - 1);
+        dma16(k + (img + key) * ld + hc + 8 * kdc[j], st + jg * 1024);
+      } else if (jg < NDMA) {
+        const int d = 8 * (jg - VK_BYTES / 1024) + vd_lo;
+        dma16(vth + (int64_t)d * vt_ld + key0 + 8 * (vchunk ^ (d & 7)), st + VK_BYTES + (jg - VK_BYTES / 1024) * 1024);
+      } else {
+        dma16(vth + key0, trash);
+      }
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.0f;
+  f32x16 oacc[3];
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+
+  const int nkb = (T + KB - 1) / KB;
+  issue(0);
+  if (nkb > 1) issue(1);
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb)
+      attn_wait_vmcnt<PER_WAVE>();
+    else
+      attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + 2 < nkb) issue(kb + 2);  // into the stage block kb-1 used
+    const uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
+    const uint8_t* vs = st + VK_BYTES;
+    const int key0 = kb * KB;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + (32 * kt + fr) * VK_PITCH + (2 * s + fg) * 16);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    if (key0 + KB > T) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3) >= T) sacc[kt][r] = kNegInf;
+    }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float mc = m_new * c;
+    float ls = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], c, -mc));
+        sacc[kt][r] = p;
+        ls += p;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    if (!__all(m_new == m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    l_run += ls;
+    m_run = m_new;
+
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kt = s >> 1, base = 8 * (s & 1);
+      f16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = (f16)sacc[kt][base + e];
+#pragma unroll
+      for (int dt = 0; dt < 3; ++dt) {
+        const int d = 32 * dt + fr;
+        const uint8_t* vrow = vs + d * VV_PITCH + 8 * fg;
+        const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow + (((2 * s) ^ (d & 7)) * 16));
+        const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + (((2 * s + 1) ^ (d & 7)) * 16));
+        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  if (qi >= T) return;
+  const float inv = 1.0f / l_run;
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d0 = 32 * dt + 8 * qd + 4 * fg;
+      if (d0 >= D) continue;
+      const float a0 = oacc[dt][4 * qd + 0] * inv, a1 = oacc[dt][4 * qd + 1] * inv;
+      const float a2 = oacc[dt][4 * qd + 2] * inv, a3 = oacc[dt][4 * qd + 3] * inv;
+      if constexpr (OUT_FP8) {
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(o) + (img + qi) * ldo + hc + d0) =
+            pack4_e4m3(a0 * out_scale, a1 * out_scale, a2 * out_scale, a3 * out_scale);
+      } else {
+        const f16x4 ov = {(f16)a0, (f16)a1, (f16)a2, (f16)a3};
+        *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(o) + (img + qi) * ldo + hc + d0) = ov;
+      }
+    }
+}
+
+template <int D>
+hipError_t launch_vt_d(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o, int64_t ldo,
+                       int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale, hipStream_t s) {
+  const int nqb = (tokens + QB - 1) / QB;
+  const int64_t blocks = (int64_t)nqb * heads * batch;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (out_fp8)
+    hipLaunchKernelGGL((flash_attn_vt_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt, vt_ld,
+                       o, ldo, tokens, heads, nqb, sl2, out_scale);
+  else
+    hipLaunchKernelGGL((flash_attn_vt_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt,
+                       vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
+  return hipGetLastError();
+}
+
 constexpr int kMapMaxT = 4096;
 
 __device__ __forceinline__ float block_max(float v, float* red) {
@@ -347,6 +570,24 @@ hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v, int6
     hipLaunchKernelGGL(flash_attn_kernel<false>, grid, dim3(256), 0, s, q, k, v, ld, o, ldo, tokens, head_dim, heads,
                        nqb, sl2, out_scale);
   return hipGetLastError();
+}
+
+bool flash_attention_vt_supported(int head_dim) { return head_dim == 64 || head_dim == 72 || head_dim == 80; }
+
+hipError_t launch_flash_attention_vt(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o,
+                                     int64_t ldo, int batch, int heads, int tokens, int head_dim, float scale,
+                                     bool out_fp8, float out_scale, hipStream_t s) {
+  if (batch < 1 || heads < 1 || tokens < 1 || !flash_attention_vt_supported(head_dim) ||
+      ld < (int64_t)heads * head_dim || (ld & 7) || ldo < (int64_t)heads * head_dim || (ldo & 3) ||
+      vt_ld < (int64_t)(tokens + KB - 1) / KB * KB || (vt_ld & 7))
+    return hipErrorInvalidValue;
+  const float sl2 = scale * 1.4426950408889634f;
+  switch (head_dim) {
+    case 64: return launch_vt_d<64>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 72: return launch_vt_d<72>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 80: return launch_vt_d<80>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv, int64_t v_offset, void* o,

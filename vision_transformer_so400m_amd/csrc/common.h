@@ -62,7 +62,9 @@ enum GemmEpi : int {
   EPI_BIAS = 0,      // acc*s + bias[n]
   EPI_BIAS_POS = 1,  // acc*s + bias[n] + pos[m % pos_rows][n]
   EPI_BIAS_RES = 2,  // acc*s + bias[n] + res[m][n]
-  EPI_BIAS_GELU = 3  // gelu(acc*s + bias[n])
+  EPI_BIAS_GELU = 3, // gelu(acc*s + bias[n])
+  EPI_QKV = 4        // acc*s + bias[n]; columns >= vt_col0 (the V part) go to
+                     // vt transposed per head instead of to c
 };
 
 struct GemmArgs {
@@ -75,6 +77,9 @@ struct GemmArgs {
   int M, N, K;                    // K in elements
   float acc_scale;                // 1 (F16) or 2^(2*exp) (FP8)
   float out_scale;                // for e4m3 outputs: 2^-exp
+  // EPI_QKV: V^T[(b*vt_heads + h)*vt_dim + d][t] at vt + row*vt_ld + t, for
+  // output row m = b*vt_tokens + t and column vt_col0 + h*vt_dim + d
+  f16* vt; int vt_col0, vt_tokens, vt_heads, vt_dim; int64_t vt_ld;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8,
@@ -92,6 +97,16 @@ hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v,
                                   int heads, int tokens, int head_dim,
                                   float scale, bool out_fp8, float out_scale,
                                   hipStream_t s);
+
+// Encoder attention with V given transposed per head: vt row (b*heads + h)*
+// head_dim + d holds keys 0..tokens-1 of that (image, head, dim), row stride
+// vt_ld >= round_up(tokens, 64), zeros in columns tokens..vt_ld-1. q and k as
+// for launch_flash_attention. head_dim must be 64, 72 or 80.
+hipError_t launch_flash_attention_vt(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld,
+                                     void* o, int64_t ldo, int batch, int heads, int tokens,
+                                     int head_dim, float scale, bool out_fp8, float out_scale,
+                                     hipStream_t s);
+bool flash_attention_vt_supported(int head_dim);
 
 hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv,
                                 int64_t v_offset, void* o, int64_t ldo,
@@ -116,6 +131,9 @@ hipError_t launch_weight_transpose(const float* w, int K, int N, void* wt,
 hipError_t launch_f32_convert(const float* x, int rows, int cols, void* y,
                               int cols_pad, bool out_fp8, float scale,
                               hipStream_t s);
+
+// Zero columns c0..c1-1 of every row of an F16 [rows, ld] matrix.
+hipError_t launch_zero_cols(f16* p, int64_t rows, int64_t ld, int c0, int c1, hipStream_t s);
 
 // Fill n 16-bit words.
 hipError_t launch_fill_u16(void* p, size_t n, uint16_t value, hipStream_t s);

@@ -88,6 +88,12 @@ __global__ __launch_bounds__(256) void f32_convert_kernel(const float* __restric
   }
 }
 
+__global__ __launch_bounds__(256) void zero_cols_kernel(f16* __restrict__ p, int64_t rows, int64_t ld, int c0, int w) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * w) return;
+  p[(i / w) * ld + c0 + (i % w)] = (f16)0.0f;
+}
+
 __global__ __launch_bounds__(256) void fill_u16_kernel(uint16_t* __restrict__ p, size_t n, uint16_t v) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -129,6 +135,14 @@ hipError_t launch_f32_convert(const float* x, int rows, int cols, void* y, int c
     hipLaunchKernelGGL(f32_convert_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, y, cols_pad, scale);
   else
     hipLaunchKernelGGL(f32_convert_kernel<false>, grid, dim3(256), 0, s, x, rows, cols, y, cols_pad, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_cols(f16* p, int64_t rows, int64_t ld, int c0, int c1, hipStream_t s) {
+  if (rows < 0 || c0 < 0 || c1 > ld || c1 < c0) return hipErrorInvalidValue;
+  const int64_t n = rows * (c1 - c0);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, rows, ld, c0, c1 - c0);
   return hipGetLastError();
 }
 

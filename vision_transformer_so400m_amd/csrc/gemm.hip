@@ -229,6 +229,20 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = gelu_tanh(v[r]);
         }
+        if constexpr (EPI == EPI_QKV) {
+          if (n >= g.vt_col0) {
+            // V part: 4 consecutive dims of one head, written transposed; the
+            // 32 lanes of a half-wave hold 32 consecutive tokens, so each of
+            // the 4 stores covers 64 contiguous bytes of a V^T row
+            const int hd = n - g.vt_col0;
+            const int hh = hd / g.vt_dim, dd = hd - hh * g.vt_dim;
+            const int bb = m / g.vt_tokens, tt = m - bb * g.vt_tokens;
+            f16* dst = g.vt + ((int64_t)(bb * g.vt_heads + hh) * g.vt_dim + dd) * g.vt_ld + tt;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[r * g.vt_ld] = (f16)v[r];
+            continue;
+          }
+        }
         if constexpr (OUT_FP8) {
           uint32_t w4 = pack4_e4m3(v[0] * g.out_scale, v[1] * g.out_scale,
                                    v[2] * g.out_scale, v[3] * g.out_scale);
@@ -273,6 +287,7 @@ hipError_t launch_epi(const GemmArgs& g, int epi, bool out_fp8, hipStream_t s) {
     case EPI_BIAS: return launch_sized<FP8, EPI_BIAS, false>(g, s);
     case EPI_BIAS_POS: return launch_sized<FP8, EPI_BIAS_POS, false>(g, s);
     case EPI_BIAS_RES: return launch_sized<FP8, EPI_BIAS_RES, false>(g, s);
+    case EPI_QKV: return launch_sized<FP8, EPI_QKV, false>(g, s);
     case EPI_BIAS_GELU:
       return out_fp8 ? launch_sized<FP8, EPI_BIAS_GELU, true>(g, s)
                      : launch_sized<FP8, EPI_BIAS_GELU, false>(g, s);
@@ -291,6 +306,9 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   if ((int64_t)g.M * g.lda * E >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   if (out_fp8 && epi != EPI_BIAS_GELU) return hipErrorInvalidValue;
+  if (epi == EPI_QKV && (!g.vt || g.vt_dim < 4 || g.vt_dim % 4 || g.vt_col0 % 4 || g.vt_tokens < 1 ||
+                         g.vt_ld < g.vt_tokens || (g.N - g.vt_col0) != g.vt_heads * g.vt_dim))
+    return hipErrorInvalidValue;
   return in_fp8 ? launch_epi<true>(g, epi, out_fp8, s) : launch_epi<false>(g, epi, out_fp8, s);
 }
 

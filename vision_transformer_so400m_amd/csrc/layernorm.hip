@@ -4,7 +4,7 @@
 // epsilon 1e-6 and affine parameters, F32 statistics computed in separate
 // sum, centered-variance and affine passes. Here one 64-lane wavefront owns
 // one row: the row is read once from HBM into registers with coalesced
-// 4-byte loads (lane i takes elements 2i, 2i+1, 2i+128, ...), the two F32
+// 16-byte loads (lane i takes 8-value chunks i, i+64, i+128), the two F32
 // reductions are wavefront shuffles, and the normalised row is written once,
 // as F16 or, when it feeds an FP8 GEMM, as e4m3 codes of y * 2^-exp (the
 // producer writes the quantized operand; page "FP8 attention and resident
@@ -16,7 +16,7 @@
 namespace siglip {
 namespace {
 
-constexpr int kMaxPairs = 16;  // width <= 2 * 64 * 16 = 2048
+constexpr int kMaxChunks = 4;  // 16-byte chunks per lane: width <= 64 * 8 * 4 = 2048
 
 template <bool OUT_FP8>
 __global__ __launch_bounds__(256) void layernorm_kernel(
@@ -26,50 +26,61 @@ __global__ __launch_bounds__(256) void layernorm_kernel(
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int pairs = width >> 1;
-  const f16x2* xr = reinterpret_cast<const f16x2*>(x + (int64_t)row * ldx);
+  const int chunks = width >> 3;  // 8 values per chunk; chunk c of the row is lane c % 64, slot c / 64
+  const f16x8* xr = reinterpret_cast<const f16x8*>(x + (int64_t)row * ldx);
 
-  float v0[kMaxPairs], v1[kMaxPairs];
+  float v[kMaxChunks][8];
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxPairs; ++i) {
-    const int p = lane + 64 * i;
-    if (p < pairs) {
-      f16x2 h = xr[p];
-      v0[i] = (float)h[0];
-      v1[i] = (float)h[1];
-    } else {
-      v0[i] = 0.0f;
-      v1[i] = 0.0f;
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      const f16x8 h = xr[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] = (float)h[e];
+        s += v[i][e];
+      }
     }
-    s += v0[i] + v1[i];
   }
   const float inv_w = 1.0f / (float)width;
   const float mean = wave_sum(s) * inv_w;
-  float c = 0.0f;
+  float cs = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kMaxPairs; ++i) {
-    if (lane + 64 * i < pairs) {
-      const float d0 = v0[i] - mean, d1 = v1[i] - mean;
-      c += d0 * d0 + d1 * d1;
+  for (int i = 0; i < kMaxChunks; ++i) {
+    if (lane + 64 * i < chunks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = v[i][e] - mean;
+        cs += d * d;
+      }
     }
   }
-  const float var = wave_sum(c) * inv_w;
+  const float var = wave_sum(cs) * inv_w;
   const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
-  for (int i = 0; i < kMaxPairs; ++i) {
-    const int p = lane + 64 * i;
-    if (p < pairs) {
-      const float2 g = reinterpret_cast<const float2*>(gamma)[p];
-      const float2 b = reinterpret_cast<const float2*>(beta)[p];
-      const float o0 = (v0[i] - mean) * rstd * g.x + b.x;
-      const float o1 = (v1[i] - mean) * rstd * g.y + b.y;
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      const f32x4 g0 = reinterpret_cast<const f32x4*>(gamma)[2 * c];
+      const f32x4 g1 = reinterpret_cast<const f32x4*>(gamma)[2 * c + 1];
+      const f32x4 b0 = reinterpret_cast<const f32x4*>(beta)[2 * c];
+      const f32x4 b1 = reinterpret_cast<const f32x4*>(beta)[2 * c + 1];
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (v[i][e] - mean) * rstd * g0[e] + b0[e];
+        o[e + 4] = (v[i][e + 4] - mean) * rstd * g1[e] + b1[e];
+      }
       if constexpr (OUT_FP8) {
-        uint32_t w = cvt_pk_e4m3(o0 * out_scale, o1 * out_scale, 0u, false);
-        reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(y) + (int64_t)row * ldy)[p] = (uint16_t)w;
+        uint32_t w0 = pack4_e4m3(o[0] * out_scale, o[1] * out_scale, o[2] * out_scale, o[3] * out_scale);
+        uint32_t w1 = pack4_e4m3(o[4] * out_scale, o[5] * out_scale, o[6] * out_scale, o[7] * out_scale);
+        reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(y) + (int64_t)row * ldy)[c] = make_uint2(w0, w1);
       } else {
-        f16x2 o = {(f16)o0, (f16)o1};
-        reinterpret_cast<f16x2*>(reinterpret_cast<f16*>(y) + (int64_t)row * ldy)[p] = o;
+        f16x8 ov;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = (f16)o[e];
+        reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(y) + (int64_t)row * ldy)[c] = ov;
       }
     }
   }
@@ -81,7 +92,8 @@ hipError_t launch_layernorm(const f16* x, int64_t ldx, void* y, int64_t ldy,
                             const float* gamma, const float* beta, int rows,
                             int width, float eps, bool out_fp8, float out_scale,
                             hipStream_t s) {
-  if (rows < 1 || width < 2 || (width & 1) || width > 2 * 64 * kMaxPairs || ldx < width || ldy < width)
+  if (rows < 1 || width < 8 || (width & 7) || width > 8 * 64 * kMaxChunks || ldx < width || ldy < width ||
+      (ldx & 7) || (ldy & 7))
     return hipErrorInvalidValue;
   dim3 grid((rows + 3) / 4);
   if (out_fp8)

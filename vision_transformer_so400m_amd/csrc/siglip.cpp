@@ -115,6 +115,8 @@ struct siglip_model {
   float op_scale = 1.0f;   // operand quantization multiplier 2^-exp
   float acc_scale = 1.0f;  // product rescale 2^(2 exp)
   int patch_pad = 0, mlp_pad = 0;
+  bool vt_path = false;  // V written transposed by the QKV GEMM for the streaming attention
+  int tokens_pad = 0;    // V^T row length: tokens rounded up to the 64-key block
 
   std::vector<void*> allocs;
   Gemm embed;
@@ -138,6 +140,7 @@ struct siglip_model {
   f16* my = nullptr;    // [B, width]
   void* ma = nullptr;   // [B, width] operand type
   void* mu = nullptr;   // [B, mlp_pad] operand type
+  f16* vt = nullptr;    // [B*heads*head_dim, tokens_pad] (vt_path only)
 
   // diagnostics
   int capture_layer = -1;
@@ -221,6 +224,36 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
   hip_check(launch_gemm(args, epi, m->fp8, out_fp8, s), "gemm launch");
 }
 
+// The fused QKV projection: Q and K row-major into qkv, V transposed per
+// head into vt when the streaming attention is used.
+void gemm_qkv(siglip_model* m, const Gemm& g, const void* a, int M, int B, hipStream_t s) {
+  if (!m->vt_path) {
+    gemm(m, g, a, m->width, M, m->qkv, 3 * m->width, EPI_BIAS, false, nullptr, 0, s);
+    return;
+  }
+  GemmArgs args{};
+  args.a = a;
+  args.lda = m->width;
+  args.w = g.w;
+  args.ldw = g.k_pad;
+  args.c = m->qkv;
+  args.ldc = 3 * m->width;
+  args.bias = g.bias;
+  args.M = M;
+  args.N = g.n_pad;
+  args.K = g.k_pad;
+  args.acc_scale = m->acc_scale;
+  args.out_scale = m->op_scale;
+  args.vt = m->vt;
+  args.vt_col0 = 2 * m->width;
+  args.vt_tokens = m->tokens;
+  args.vt_heads = m->heads;
+  args.vt_dim = m->head_dim;
+  args.vt_ld = m->tokens_pad;
+  (void)B;
+  hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "qkv gemm launch");
+}
+
 void capture(siglip_model* m, int stage, const void* src, size_t bytes, hipStream_t s) {
   if (m->capture_layer < 0 || !m->cap[stage]) return;
   hip_check(hipMemcpyAsync(m->cap[stage], src, bytes, hipMemcpyDeviceToDevice, s), "capture copy");
@@ -235,7 +268,12 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
   switch (stage) {
     case SIGLIP_STAGE_EMBED: case SIGLIP_STAGE_H_ATTN: case SIGLIP_STAGE_H_OUT: break;
     case SIGLIP_STAGE_LN1: case SIGLIP_STAGE_ATTN: case SIGLIP_STAGE_LN2: case SIGLIP_STAGE_FINAL_LN: b = e; break;
-    case SIGLIP_STAGE_QKV: c = l = 3LL * m->width; break;
+    case SIGLIP_STAGE_QKV: l = 3LL * m->width; c = m->vt_path ? 2LL * m->width : l; break;
+    case SIGLIP_STAGE_V_T:
+      r = m->vt_path ? (int64_t)batch * m->heads * m->head_dim : 0;
+      c = m->tokens;
+      l = m->tokens_pad;
+      break;
     case SIGLIP_STAGE_MLP_HIDDEN: c = m->mlp; l = m->mlp_pad; b = e; break;
     case SIGLIP_STAGE_MAP_KV: c = l = 2LL * m->width; break;
     case SIGLIP_STAGE_MAP_ATTN: case SIGLIP_STAGE_MAP_LN: r = batch; b = e; break;
@@ -300,6 +338,12 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     LaunchTimer lt(m, SIGLIP_K_EMBED, s);
     gemm(m, m->embed, m->xp, m->patch_pad, M, m->h, W, EPI_BIAS_POS, false, nullptr, 0, s);
   }
+  if (m->vt_path && m->tokens_pad > m->tokens) {
+    // V^T columns past the last token are read by the last key block: zeros
+    LaunchTimer lt(m, SIGLIP_K_INPUT, s);
+    hip_check(launch_zero_cols(m->vt, (int64_t)B * m->heads * m->head_dim, m->tokens_pad, m->tokens, m->tokens_pad, s),
+              "zero V^T tail");
+  }
   if (cap) capture(m, SIGLIP_STAGE_EMBED, m->h, cb(SIGLIP_STAGE_EMBED), s);
 
   const float attn_scale = 1.0f / std::sqrt((float)m->head_dim);
@@ -313,14 +357,20 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     if (ci) capture(m, SIGLIP_STAGE_LN1, m->a, cb(SIGLIP_STAGE_LN1), s);
     {
       LaunchTimer lt(m, SIGLIP_K_QKV, s);
-      gemm(m, Ly.qkv, m->a, W, M, m->qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm_qkv(m, Ly.qkv, m->a, M, B, s);
     }
     if (ci) capture(m, SIGLIP_STAGE_QKV, m->qkv, cb(SIGLIP_STAGE_QKV), s);
+    if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, m->vt, cb(SIGLIP_STAGE_V_T), s);
     {
       LaunchTimer lt(m, SIGLIP_K_ATTENTION, s);
-      hip_check(launch_flash_attention(m->qkv, m->qkv + W, m->qkv + 2 * W, 3 * W, m->o, W, B, m->heads, m->tokens,
-                                       m->head_dim, attn_scale, q8, m->op_scale, s),
-                "attention");
+      if (m->vt_path)
+        hip_check(launch_flash_attention_vt(m->qkv, m->qkv + W, 3 * W, m->vt, m->tokens_pad, m->o, W, B, m->heads,
+                                            m->tokens, m->head_dim, attn_scale, q8, m->op_scale, s),
+                  "attention");
+      else
+        hip_check(launch_flash_attention(m->qkv, m->qkv + W, m->qkv + 2 * W, 3 * W, m->o, W, B, m->heads, m->tokens,
+                                         m->head_dim, attn_scale, q8, m->op_scale, s),
+                  "attention");
     }
     if (ci) capture(m, SIGLIP_STAGE_ATTN, m->o, cb(SIGLIP_STAGE_ATTN), s);
     {
@@ -513,6 +563,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->acc_scale = std::ldexp(1.0f, 2 * m->scale_exp);
     m->patch_pad = (int)round_up(P, kKAlign);
     m->mlp_pad = (int)round_up(F, kNAlign);  // U is both an N (MLP up) and a K (MLP down) dimension
+    m->vt_path = flash_attention_vt_supported(m->head_dim);
+    m->tokens_pad = (int)round_up(T, 64);
 
     const size_t staging_floats = (size_t)std::max<int64_t>({(int64_t)P * W, 3LL * W * W, (int64_t)W * F, (int64_t)T * W});
     float* staging = static_cast<float*>(m->dalloc(staging_floats * 4));
@@ -551,6 +603,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
         {&m->xp, M * m->patch_pad * es}, {(void**)&m->h, M * W * 2}, {&m->a, M * W * es},
         {(void**)&m->qkv, M * 3 * W * 2}, {&m->o, M * W * es}, {&m->u, M * m->mlp_pad * es},
         {&m->mo, B * W * es}, {(void**)&m->my, B * W * 2}, {&m->ma, B * W * es}, {&m->mu, B * m->mlp_pad * es},
+        {(void**)&m->vt, m->vt_path ? B * W * m->tokens_pad * 2 : 0},
     };
     size_t total = 0;
     for (auto& p : parts) total += (size_t)round_up(p.bytes, 256);
