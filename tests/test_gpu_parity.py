@@ -143,9 +143,12 @@ def _attn_ref(q, k, v, heads, d, scale):
 
 
 def _attn_extra(v, heads, d):
-    # probability rounding to F16 before PV: 2^-11 * max|v| of the head
+    # probabilities are rounded to F16 (relative error <= 2^-11) before the PV
+    # product; with the normaliser summed either from the exact or from the
+    # rounded probabilities the output moves by at most 2^-11 * max|v - o|
+    # <= 2^-10 * max|v| of the head
     vh = np.abs(O.split_heads(v.astype(np.float64), heads)).max(axis=(-1, -2), keepdims=True)
-    return O.merge_heads(np.broadcast_to(vh, vh.shape[:-2] + (v.shape[1], d))) * 2.0 ** -11
+    return O.merge_heads(np.broadcast_to(vh, vh.shape[:-2] + (v.shape[1], d))) * 2.0 ** -10
 
 
 @pytest.mark.parametrize("t", [1, 4, 63, 64, 65, 127, 128, 129, 300])
@@ -205,7 +208,7 @@ def test_attention_c2_full_size_sampled(V):
         sl = slice(hi * d, (hi + 1) * d)
         ref = O.attention(q[bi, :, sl].astype(np.float64), k[bi, :, sl].astype(np.float64),
                           v[bi, :, sl].astype(np.float64), 1 / math.sqrt(d))
-        extra = np.abs(v[bi, :, sl].astype(np.float64)).max() * 2.0 ** -11 + 1e-6
+        extra = np.abs(v[bi, :, sl].astype(np.float64)).max() * 2.0 ** -10 + 1e-6
         assert_close(f"c2 b{bi} h{hi}", o[bi, :, sl], ref, extra=extra)
 
 

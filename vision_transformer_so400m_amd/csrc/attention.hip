@@ -256,16 +256,30 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(
 // global -> LDS with global_load_lds_dwordx4 into a 3-stage ring, exactly as
 // the GEMM operands do: no register staging and no transposition here.
 //
-// LDS stage (bytes): K [64 keys x 176] (11 chunks of 16 B per key: 9 chunks of
+// LDS stage (bytes): K [64 rows x 176] (11 chunks of 16 B per key: 9 chunks of
 // dims, then copies of the last dim chunk, which meet the zero Q padding), then
-// V^T [96 dims x 128] (64 keys per row, 16-byte chunk index XOR (dim & 7);
-// rows D..95 are zeros written once). Keys past T read token T-1 (finite,
-// masked to -inf); V^T columns past T are zeros in memory.
+// V^T [96 dims x 128] (64 keys per row, 16-byte chunk index XOR-swizzled as in
+// the GEMM; row D is ones and rows D+1..95 zeros, written once). Keys past T
+// read token T-1 (finite, masked to -inf); V^T columns past T are zeros in
+// memory.
+//
+// K rows are stored permuted within each 16-row group (rows 4..7 hold keys
+// 8..11 and rows 8..11 keys 4..7). The S^T result puts tile rows
+// 16s + 8(e/4) + 4g + e%4 in element e of lane group g; with the permutation
+// those are keys 16s + 8g + e, eight consecutive keys, so each V^T fragment
+// of the PV product is one 16-byte LDS read.
 constexpr int VK_PITCH = 176;
 constexpr int VK_BYTES = KB * VK_PITCH;          // 11 x 1 KiB
 constexpr int VV_PITCH = 128;
 constexpr int VT_STAGE = VK_BYTES + VROWS * VV_PITCH;
 constexpr int VT_STAGES = 3;
+
+// key held by K tile row i (see the permutation above)
+__device__ __forceinline__ int key_of_row(int i) {
+  const int x = i & 15;
+  return (i & ~15) + ((x >= 4 && x < 8) ? x + 4 : (x >= 8 && x < 12) ? x - 4 : x);
+}
+__device__ __forceinline__ int vswz_key(int d) { return (d & 7) ^ ((d >> 3) & 1); }
 
 template <int N>
 __device__ __forceinline__ void attn_wait_vmcnt() {
@@ -279,14 +293,17 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
   constexpr int NDC = D / 8;                     // 16-byte dim chunks per key
-  constexpr int NDMA = VK_BYTES / 1024 + D / 8;  // 1 KiB transfers per stage
+  constexpr int NK = VK_BYTES / 1024;            // 1 KiB transfers for K per stage
+  constexpr int NDMA = NK + D / 8;               // 1 KiB transfers per stage
   constexpr int PER_WAVE = (NDMA + 3) / 4;       // every wave issues the same count
+  constexpr int RL = (D - 64) / 2;               // oacc[2] register holding O^T row D (lane group 0)
+  constexpr float kTau = 8.0f;                   // rescale only when a row max grows by > 2^8
   __shared__ __attribute__((aligned(1024))) uint8_t smem[VT_STAGES * VT_STAGE + 1024];
   uint8_t* trash = smem + VT_STAGES * VT_STAGE;  // target of the padding transfers
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int fr = lane & 31;
   const int fg = lane >> 5;
   const int L = xcd_block(blockIdx.x, gridDim.x);
@@ -308,44 +325,65 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
     else
       qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  // zero V^T rows D..95 of every stage once
+  // constant V^T rows of every stage: row D = 1 (the PV product then also
+  // yields each query's sum of the F16 probabilities it used), rows D+1..95 = 0
   constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
   for (int i = t; i < VT_STAGES * ZCH; i += 256) {
-    uint8_t* z = smem + (i / ZCH) * VT_STAGE + VK_BYTES + D * VV_PITCH + (i % ZCH) * 16;
-    *reinterpret_cast<i32x4*>(z) = i32x4{0, 0, 0, 0};
+    const int r = i % ZCH;
+    uint8_t* z = smem + (i / ZCH) * VT_STAGE + VK_BYTES + D * VV_PITCH + r * 16;
+    const int one = 0x3C003C00;  // two F16 ones
+    *reinterpret_cast<i32x4*>(z) = r < VV_PITCH / 16 ? i32x4{one, one, one, one} : i32x4{0, 0, 0, 0};
   }
   __syncthreads();
 
-  // transfer slot j of this wave: global index jg = wave + 4 j
-  int krow[PER_WAVE], kdc[PER_WAVE];
+  // ---- transfer slots (slot j of this wave: global index jg = wave + 4 j).
+  // Sources are kept without the block offset: a K slot advances by key0 rows,
+  // a V^T slot by key0 columns, a padding slot not at all.
+  const f16* src[PER_WAVE];
+  int kkey[PER_WAVE], kdc[PER_WAVE];
+  const int vd_lo = lane >> 3;
+  const int vchunk = lane & 7;
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int jg = wave + 4 * j;
     const int off = jg * 1024 + 16 * lane;
-    krow[j] = off / VK_PITCH;
+    kkey[j] = key_of_row(off / VK_PITCH);
     kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
+    if (jg < NK) {
+      src[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
+    } else if (jg < NDMA) {
+      const int d = 8 * (jg - NK) + vd_lo;
+      src[j] = vth + (int64_t)d * vt_ld + 8 * (vchunk ^ vswz_key(d));
+    } else {
+      src[j] = vth;
+    }
   }
-  const int vd_lo = lane >> 3;                 // V^T row within a transfer
-  const int vchunk = (lane & 7);               // physical chunk of this lane
   auto issue = [&](int kb) {
     const int key0 = kb * KB;
     uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
+    const bool tail = key0 + KB > T;  // keys past T re-read token T-1
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int jg = wave + 4 * j;
-      if (jg < VK_BYTES / 1024) {
-        const int key = min(key0 + krow[j], T - 1);
-        dma16(k + (img + key) * ld + hc + 8 * kdc[j], st + jg * 1024);
+      if (jg < NK) {
+        const f16* p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
+                            : src[j] + (int64_t)key0 * ld;
+        dma16(p, st + jg * 1024);
       } else if (jg < NDMA) {
-        const int d = 8 * (jg - VK_BYTES / 1024) + vd_lo;
-        dma16(vth + (int64_t)d * vt_ld + key0 + 8 * (vchunk ^ (d & 7)), st + VK_BYTES + (jg - VK_BYTES / 1024) * 1024);
+        dma16(src[j] + key0, st + VK_BYTES + (jg - NK) * 1024);
       } else {
-        dma16(vth + key0, trash);
+        dma16(src[j], trash);
       }
     }
   };
 
-  float m_run = kNegInf, l_run = 0.0f;
+  // per-lane LDS byte offsets of the fragments inside a stage
+  const int koff = fr * VK_PITCH + fg * 16;                      // + kt*32*176 + s*32
+  int voff[4];                                                   // + dt*32*128
+#pragma unroll
+  for (int s = 0; s < 4; ++s) voff[s] = VK_BYTES + fr * VV_PITCH + 16 * ((2 * s + fg) ^ vswz_key(fr));
+
+  float m_run = kNegInf;
   f32x16 oacc[3];
 #pragma unroll
   for (int dt = 0; dt < 3; ++dt)
@@ -363,7 +401,6 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
     __builtin_amdgcn_s_barrier();
     if (kb + 2 < nkb) issue(kb + 2);  // into the stage block kb-1 used
     const uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
-    const uint8_t* vs = st + VK_BYTES;
     const int key0 = kb * KB;
 
     f32x16 sacc[2];
@@ -373,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + (32 * kt + fr) * VK_PITCH + (2 * s + fg) * 16);
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
       }
     }
@@ -382,57 +419,58 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (key0 + 32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3) >= T) sacc[kt][r] = kNegInf;
+          if (key0 + key_of_row(32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3)) >= T) sacc[kt][r] = kNegInf;
     }
-    float mx = kNegInf;
+    float mx;
+    {
+      float a[8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float mc = m_new * c;
-    float ls = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], c, -mc));
-        sacc[kt][r] = p;
-        ls += p;
-      }
-    ls += __shfl_xor(ls, 32, 64);
-    if (!__all(m_new == m_run)) {
+      for (int i = 0; i < 8; ++i)
+        a[i] = fmaxf(fmaxf(sacc[0][i], sacc[0][i + 8]), fmaxf(sacc[1][i], sacc[1][i + 8]));
+      mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+    // Probabilities are exp(scale (s - m_run)) with a running reference m_run
+    // that only moves when a row maximum exceeds it by more than 2^8 in
+    // exp2 units, so they stay <= 2^8; the final division by the row sum
+    // makes the result independent of the reference.
+    if (__any((mx - m_run) * c > kTau)) {
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 3; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      m_run = m_new;
     }
-    l_run += ls;
-    m_run = m_new;
+    const float mc = m_run * c;
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kt = s >> 1, base = 8 * (s & 1);
       f16x8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (f16)sacc[kt][base + e];
+      for (int e = 0; e < 8; e += 2) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sacc[kt][base + e], c, -mc)),
+                          __builtin_amdgcn_exp2f(fmaf(sacc[kt][base + e + 1], c, -mc))};
+        const f16x2 ph = __builtin_convertvector(pp, f16x2);
+        pf[e] = ph[0];
+        pf[e + 1] = ph[1];
+      }
 #pragma unroll
-      for (int dt = 0; dt < 3; ++dt) {
-        const int d = 32 * dt + fr;
-        const uint8_t* vrow = vs + d * VV_PITCH + 8 * fg;
-        const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow + (((2 * s) ^ (d & 7)) * 16));
-        const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + (((2 * s + 1) ^ (d & 7)) * 16));
-        const f16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int dt = 0; dt < 3; ++dt) {  // keys 16s + 8fg + (0..7) of dim row 32dt + fr
+        const f16x8 vf = *reinterpret_cast<const f16x8*>(st + voff[s] + dt * 32 * VV_PITCH);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[dt], 0, 0, 0);
       }
     }
   }
 
+  // the row sum sits in O^T row D, register RL of lane group 0
+  const float lsum0 = oacc[2][RL];
+  const float lsum1 = __shfl_xor(lsum0, 32, 64);
   if (qi >= T) return;
-  const float inv = 1.0f / l_run;
+  const float inv = 1.0f / (fg ? lsum1 : lsum0);
 #pragma unroll
   for (int dt = 0; dt < 3; ++dt)
 #pragma unroll

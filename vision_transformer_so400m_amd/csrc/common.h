@@ -21,8 +21,8 @@ constexpr float kE4m3Max = 448.0f;
 // low (hi=false) or high (hi=true) 16 bits of `old`. Inputs are clamped to
 // +-448 first so out-of-range values saturate instead of becoming NaN.
 __device__ __forceinline__ uint32_t cvt_pk_e4m3(float a, float b, uint32_t old, bool hi) {
-  a = fminf(fmaxf(a, -kE4m3Max), kE4m3Max);
-  b = fminf(fmaxf(b, -kE4m3Max), kE4m3Max);
+  a = __builtin_amdgcn_fmed3f(a, -kE4m3Max, kE4m3Max);
+  b = __builtin_amdgcn_fmed3f(b, -kE4m3Max, kE4m3Max);
   return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, true)
             : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, false);
 }
@@ -44,14 +44,17 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
-// tanh(u) = 1 - 2 / (exp(2u) + 1) evaluated through exp2.
+// GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). Since
+// 0.5 (1 + tanh(z)) = 1 / (1 + exp(-2z)), this is x / (1 + exp(-2z)) with
+// z = sqrt(2/pi) x (1 + 0.044715 x^2): one exp2 and one reciprocal (both
+// hardware approximations, ~1 ulp of F32), no IEEE division. Large negative x
+// gives exp2 -> inf and x * rcp(inf) = -0; large positive x gives x.
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float k2 = 2.0f * 0.7978845608028654f * 1.4426950408889634f;  // 2*sqrt(2/pi)*log2(e)
-  float u = x + 0.044715f * x * x * x;
-  float e = __builtin_amdgcn_exp2f(k2 * u);   // exp(2*sqrt(2/pi)*u)
-  float t = 1.0f - 2.0f / (e + 1.0f);         // saturates to +-1 for large |u|
-  return 0.5f * x * (1.0f + t);
+  const float k = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float x2 = x * x;
+  const float z = x * fmaf(0.044715f, x2, 1.0f);
+  const float e = __builtin_amdgcn_exp2f(k * z);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -80,6 +83,7 @@ struct GemmArgs {
   // EPI_QKV: V^T[(b*vt_heads + h)*vt_dim + d][t] at vt + row*vt_ld + t, for
   // output row m = b*vt_tokens + t and column vt_col0 + h*vt_dim + d
   f16* vt; int vt_col0, vt_tokens, vt_heads, vt_dim; int64_t vt_ld;
+  float vt_inv_dim;  // 1 / vt_dim
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8,

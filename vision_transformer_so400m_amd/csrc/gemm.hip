@@ -15,11 +15,11 @@
 // operand scale is folded into acc_scale). F32 accumulation.
 //
 // Tiling: a workgroup of 4 or 8 waves owns a BM x BN output tile and walks K in
-// 128-byte slices (64 F16 or 128 e4m3 values per row). Slices are staged
-// global -> registers -> LDS, double-buffered so the loads of slice k+1 are in
-// flight while slice k is multiplied. LDS rows are 128 bytes with the 16-byte
-// chunk index XOR-swizzled by (row & 7), so the 32 lanes that read one chunk
-// column of 32 consecutive rows hit distinct banks.
+// 128-byte slices (64 F16 or 128 e4m3 values per row). Slices go global ->
+// LDS directly (global_load_lds_dwordx4) into a ring of STAGES buffers, so the
+// loads of the next slices are in flight while one is multiplied. LDS rows are
+// 128 bytes with the 16-byte chunk index XOR-swizzled (swz below), so the 16
+// lanes that read one chunk of 16 consecutive rows hit distinct banks.
 //
 // The MFMA is issued with the weight fragment as its first operand, so the
 // hardware's 32x32 result holds, per lane, one activation row m and four
@@ -46,7 +46,13 @@ struct Tile {
   static constexpr int STAGE = (BM + BN) * kRowBytes;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// 16-byte chunk swizzle of a 128-byte LDS row. A fragment read has 16 lanes
+// reading one logical chunk of 16 consecutive rows; with 64 banks of 4 bytes
+// two 128-byte rows span all banks, so (row & 1) picks the half and the chunk
+// must differ across the 8 rows of each parity: chunk ^ (row & 7) ^ ((row >> 3)
+// & 1) does that (and is also a bijection on any 8 aligned rows).
+__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
 
 // Linear workgroup id -> output tile. Workgroups are dispatched round-robin
 // over the 8 XCDs (id % 8), each with its own L2. The remap gives every XCD
@@ -98,11 +104,12 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
   // BN rows of Wt, 128 bytes each, chunk-swizzled. Transfer j of wave w
   // fills tile rows R j + 8 w .. +7 (R = 8 x waves); lane i lands at row
   // R j + 8 w + i/8, physical chunk i%8, so it fetches logical chunk
-  // (i%8) ^ (i/8).
+  // (i%8) ^ swz_key(row).
   constexpr int R = T::ROWS_PER_ROUND;
   constexpr int CH = (BM + BN) / R;  // transfers per thread per stage
   const int rr = lane >> 3;
-  const int lchunk = (lane & 7) ^ rr;
+  // tile row R j + 8 w + rr: swz_key = rr ^ ((R j / 8 + w) & 1) = rr ^ (w & 1), as R j / 8 is even
+  const int lchunk = (lane & 7) ^ rr ^ (wave & 1);
   const uint8_t* src[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
@@ -202,6 +209,36 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
   }
 
   // ---- epilogue: lane holds row m = tile row + fr, columns 8q + 4fg + (0..3)
+  if constexpr (EPI == EPI_QKV) {
+    if (n0 + wn * WN >= g.vt_col0) {
+      // V columns (whole waves: vt_col0 is a multiple of 128): 4 consecutive
+      // dims of one head written transposed. The 32 lanes of a half-wave hold
+      // 32 consecutive tokens, so each store covers 64 contiguous bytes of a
+      // V^T row.
+#pragma unroll
+      for (int i = 0; i < T::TM; ++i) {
+        const int m = m0 + wm * WM + i * 32 + fr;
+        if (m >= g.M) continue;
+        const int bb = m / g.vt_tokens, tt = m - bb * g.vt_tokens;
+        f16* vrow0 = g.vt + (int64_t)bb * g.vt_heads * g.vt_dim * g.vt_ld + tt;
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int n = n0 + wn * WN + j * 32 + 8 * qq + 4 * fg;
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(g.bias + n);
+            const int hd = n - g.vt_col0;  // head*dim + d; the 4 dims never cross a head (dim % 4 == 0)
+            const int hh = (int)(((float)hd + 0.5f) * g.vt_inv_dim);  // exact: hd < 2^20, dim <= 2^10
+            const int dd = hd - hh * g.vt_dim;
+            f16* dst = vrow0 + ((int64_t)hh * g.vt_dim + dd) * g.vt_ld;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[r * g.vt_ld] = (f16)(acc[i][j][4 * qq + r] * g.acc_scale + bv[r]);
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) {
     const int m = m0 + wm * WM + i * 32 + fr;
@@ -228,20 +265,6 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
         if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = gelu_tanh(v[r]);
-        }
-        if constexpr (EPI == EPI_QKV) {
-          if (n >= g.vt_col0) {
-            // V part: 4 consecutive dims of one head, written transposed; the
-            // 32 lanes of a half-wave hold 32 consecutive tokens, so each of
-            // the 4 stores covers 64 contiguous bytes of a V^T row
-            const int hd = n - g.vt_col0;
-            const int hh = hd / g.vt_dim, dd = hd - hh * g.vt_dim;
-            const int bb = m / g.vt_tokens, tt = m - bb * g.vt_tokens;
-            f16* dst = g.vt + ((int64_t)(bb * g.vt_heads + hh) * g.vt_dim + dd) * g.vt_ld + tt;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r * g.vt_ld] = (f16)v[r];
-            continue;
-          }
         }
         if constexpr (OUT_FP8) {
           uint32_t w4 = pack4_e4m3(v[0] * g.out_scale, v[1] * g.out_scale,
@@ -306,8 +329,9 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   if ((int64_t)g.M * g.lda * E >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   if (out_fp8 && epi != EPI_BIAS_GELU) return hipErrorInvalidValue;
-  if (epi == EPI_QKV && (!g.vt || g.vt_dim < 4 || g.vt_dim % 4 || g.vt_col0 % 4 || g.vt_tokens < 1 ||
-                         g.vt_ld < g.vt_tokens || (g.N - g.vt_col0) != g.vt_heads * g.vt_dim))
+  if (epi == EPI_QKV && (!g.vt || g.vt_dim < 4 || g.vt_dim % 4 || g.vt_dim > 1024 || g.vt_col0 % 128 ||
+                         g.vt_tokens < 1 || g.vt_ld < g.vt_tokens || g.N >= (1 << 20) ||
+                         (g.N - g.vt_col0) != g.vt_heads * g.vt_dim))
     return hipErrorInvalidValue;
   return in_fp8 ? launch_epi<true>(g, epi, out_fp8, s) : launch_epi<false>(g, epi, out_fp8, s);
 }

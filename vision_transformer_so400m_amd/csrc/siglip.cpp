@@ -250,6 +250,7 @@ void gemm_qkv(siglip_model* m, const Gemm& g, const void* a, int M, int B, hipSt
   args.vt_heads = m->heads;
   args.vt_dim = m->head_dim;
   args.vt_ld = m->tokens_pad;
+  args.vt_inv_dim = 1.0f / (float)m->head_dim;
   (void)B;
   hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "qkv gemm launch");
 }
