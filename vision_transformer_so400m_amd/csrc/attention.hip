@@ -272,7 +272,7 @@ constexpr int VK_PITCH = 176;
 constexpr int VK_BYTES = KB * VK_PITCH;          // 11 x 1 KiB
 constexpr int VV_PITCH = 128;
 constexpr int VT_STAGE = VK_BYTES + VROWS * VV_PITCH;
-constexpr int VT_STAGES = 3;
+constexpr int VT_STAGES_DEFAULT = 2;  // 48 KiB per workgroup: three workgroups per CU
 
 // key held by K tile row i (see the permutation above)
 __device__ __forceinline__ int key_of_row(int i) {
@@ -287,8 +287,8 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, bool OUT_FP8>
-__global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
+template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3>
+__global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
@@ -325,6 +325,11 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
     else
       qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
+  // The Q fragments must be complete before the block loop: an explicit,
+  // compiler-visible wait here keeps the compiler from inserting a full
+  // vmcnt(0) before the first MFMA of every block, which would also drain
+  // the transfers prefetching later blocks.
+  __builtin_amdgcn_s_waitcnt(0);
   // constant V^T rows of every stage: row D = 1 (the PV product then also
   // yields each query's sum of the F16 probabilities it used), rows D+1..95 = 0
   constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
@@ -391,15 +396,16 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt_kernel(
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
 
   const int nkb = (T + KB - 1) / KB;
-  issue(0);
-  if (nkb > 1) issue(1);
+#pragma unroll
+  for (int p = 0; p < VT_STAGES - 1; ++p)
+    if (p < nkb) issue(p);
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb)
-      attn_wait_vmcnt<PER_WAVE>();
+    if (kb + VT_STAGES - 2 < nkb)
+      attn_wait_vmcnt<(VT_STAGES - 2) * PER_WAVE>();
     else
       attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kb + 2 < nkb) issue(kb + 2);  // into the stage block kb-1 used
+    if (kb + VT_STAGES - 1 < nkb) issue(kb + VT_STAGES - 1);  // into the stage block kb-1 used
     const uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
     const int key0 = kb * KB;
 

@@ -290,15 +290,15 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
 
 template <bool FP8, int EPI, bool OUT_FP8>
 hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
-  // Tile choice measured on the batch-64 shapes (M = 46,656): eight-wave
-  // 256-row tiles (two waves per SIMD, 128x64 or 64x64 per wave) for wide N,
-  // four-wave 128x128 tiles with two LDS stages (two workgroups per CU) for
-  // N = 1152; small M falls back to tiles that still fill the 256 CUs.
+  // Tile choice measured on the batch-64 shapes (M = 46,656): N divisible by
+  // 256 takes 256x256 tiles of eight waves (128x64 each, one workgroup per
+  // CU); the others take 128x128 tiles of eight waves (64x32 each) with two
+  // LDS stages, two workgroups per CU. Small M falls back to tiles that still
+  // fill the 256 CUs.
   const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
   if (tiles_128 >= 1024) {
     if (g.N % 256 == 0) return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(g, s);
-    if (g.N >= 2048) return launch_cfg<256, 128, 64, 64, FP8 ? 2 : 3, FP8, EPI, OUT_FP8>(g, s);
-    return launch_cfg<128, 128, 64, 64, 2, FP8, EPI, OUT_FP8>(g, s);
+    return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8>(g, s);
   }
   if (tiles_128 >= 384) return launch_cfg<128, 128, 64, 64, 2, FP8, EPI, OUT_FP8>(g, s);
   return launch_cfg<64, 64, 32, 32, 3, FP8, EPI, OUT_FP8>(g, s);
