@@ -222,11 +222,13 @@ typedef enum {
   SIGLIP_K_COUNT = 11
 } siglip_kernel_class;
 
-/* Turn per-launch timing on (enable != 0) or off for later siglip_encode
- * calls on this model, and reset the totals. While on, every launch is
- * bracketed by two HIP events recorded on the call's stream, so a launch's
- * duration is the time between them on the GPU. Errors: INVALID_ARG. */
-SIGLIP_API int siglip_debug_timing(siglip_model* m, int32_t enable);
+/* Per-launch timing of later siglip_encode calls on this model, and reset of
+ * the totals. class_mask bit k (1 << siglip_kernel_class) selects the
+ * launches of class k; 0 turns timing off. Each selected launch is bracketed
+ * by two HIP events recorded on the call's stream, so its duration is the
+ * time between them on the GPU; unselected launches are not perturbed.
+ * Errors: INVALID_ARG. */
+SIGLIP_API int siglip_debug_timing(siglip_model* m, uint32_t class_mask);
 
 /* Totals since timing was turned on for one kernel class: summed launch
  * durations in milliseconds and the number of launches. Waits for the

@@ -452,3 +452,21 @@ def test_c4_27_layers_fp8_b64_sampled(V):
     _flush(f"  c4 vs unquantized oracle: cosine {cos.min():.6f}, max abs {mx.max():.4e}; "
            f"vs e4m3-operand oracle: cosine {cq.min():.6f}, max abs {mq.max():.4e}")
     assert cos.min() >= 0.99 and mx.max() <= 0.5
+
+
+def test_launch_timing_hook_counts_only_selected_classes(V):
+    dims = S.four_token_dims(1)
+    model, _ = make_model(V, dims, 0, max_batch=2)
+    x = torch.from_numpy(S.make_pixels(dims, 2, 0)).cuda()
+    model.debug_timing(["MLP_UP", "ATTENTION"])
+    for _ in range(3):
+        model.encode(x)
+    torch.cuda.synchronize()
+    ms_up, n_up = model.debug_timing_read("MLP_UP")
+    ms_at, n_at = model.debug_timing_read("ATTENTION")
+    ms_qkv, n_qkv = model.debug_timing_read("QKV")
+    assert (n_up, n_at, n_qkv) == (3, 3, 0) and ms_up > 0 and ms_at > 0
+    model.debug_timing(False)
+    model.encode(x)
+    torch.cuda.synchronize()
+    assert model.debug_timing_read("MLP_UP") == (0.0, 0)

@@ -75,7 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.siglip_debug_stage_info.argtypes = [vp, i32, P(i64), P(i64), P(i64), P(i32)]
     lib.siglip_debug_stage.argtypes = [vp, i32, vp, ctypes.c_size_t]
     lib.siglip_debug_fill_workspace.argtypes = [vp, ctypes.c_uint16]
-    lib.siglip_debug_timing.argtypes = [vp, i32]
+    lib.siglip_debug_timing.argtypes = [vp, ctypes.c_uint32]
     lib.siglip_debug_timing_read.argtypes = [vp, i32, P(ctypes.c_double), P(i64)]
     for name in EXPORTED:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
@@ -175,9 +175,19 @@ class Model:
     def debug_fill_workspace(self, pattern: int) -> None:
         _check(load_library().siglip_debug_fill_workspace(self.handle, pattern))
 
-    def debug_timing(self, enable: bool) -> None:
-        """Per-launch HIP-event timing of later encode calls (resets totals)."""
-        _check(load_library().siglip_debug_timing(self.handle, 1 if enable else 0))
+    def debug_timing(self, classes) -> None:
+        """Per-launch HIP-event timing of later encode calls for the given
+        kernel classes (names or indices; True = all, False/None/() = off).
+        Resets the totals."""
+        if classes is True:
+            mask = (1 << len(KERNEL_CLASSES)) - 1
+        elif not classes:
+            mask = 0
+        else:
+            mask = 0
+            for c in classes:
+                mask |= 1 << (KCLASS[c] if isinstance(c, str) else int(c))
+        _check(load_library().siglip_debug_timing(self.handle, mask))
 
     def debug_timing_read(self, kclass) -> tuple:
         """(total ms, launches) of one kernel class since timing was enabled."""

@@ -287,16 +287,18 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3>
+template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1>
 __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
+  static_assert(QT == 1 || QT == 2, "query tiles per wave");
+  constexpr int QWG = 4 * 32 * QT;               // queries per workgroup
   constexpr int NDC = D / 8;                     // 16-byte dim chunks per key
   constexpr int NK = VK_BYTES / 1024;            // 1 KiB transfers for K per stage
   constexpr int NDMA = NK + D / 8;               // 1 KiB transfers per stage
   constexpr int PER_WAVE = (NDMA + 3) / 4;       // every wave issues the same count
-  constexpr int RL = (D - 64) / 2;               // oacc[2] register holding O^T row D (lane group 0)
+  constexpr int RL = (D - 64) / 2;               // oacc[.][2] register holding O^T row D (lane group 0)
   constexpr float kTau = 8.0f;                   // rescale only when a row max grows by > 2^8
   __shared__ __attribute__((aligned(1024))) uint8_t smem[VT_STAGES * VT_STAGE + 1024];
   uint8_t* trash = smem + VT_STAGES * VT_STAGE;  // target of the padding transfers
@@ -313,18 +315,22 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   const int b = bh / H;
   const int hc = h * D;
   const int64_t img = (int64_t)b * T;
-  const int qi = qb * QB + wave * 32 + fr;
+  int qi[QT];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) qi[u] = qb * QWG + (wave * QT + u) * 32 + fr;
   const f16* vth = vt + (int64_t)bh * D * vt_ld;  // this head's V^T rows
 
-  f16x8 qf[5];
+  f16x8 qf[QT][5];
 #pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    const int d0 = 16 * s + 8 * fg;
-    if (qi < T && d0 < D)
-      qf[s] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
-    else
-      qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
+  for (int u = 0; u < QT; ++u)
+#pragma unroll
+    for (int s = 0; s < 5; ++s) {
+      const int d0 = 16 * s + 8 * fg;
+      if (qi[u] < T && d0 < D)
+        qf[u][s] = *reinterpret_cast<const f16x8*>(q + (img + qi[u]) * ld + hc + d0);
+      else
+        qf[u][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   // The Q fragments must be complete before the block loop: an explicit,
   // compiler-visible wait here keeps the compiler from inserting a full
   // vmcnt(0) before the first MFMA of every block, which would also drain
@@ -388,12 +394,16 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
 #pragma unroll
   for (int s = 0; s < 4; ++s) voff[s] = VK_BYTES + fr * VV_PITCH + 16 * ((2 * s + fg) ^ vswz_key(fr));
 
-  float m_run = kNegInf;
-  f32x16 oacc[3];
+  float m_run[QT];
+  f32x16 oacc[QT][3];
 #pragma unroll
-  for (int dt = 0; dt < 3; ++dt)
+  for (int u = 0; u < QT; ++u) {
+    m_run[u] = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+    for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[u][dt][r] = 0.0f;
+  }
 
   const int nkb = (T + KB - 1) / KB;
 #pragma unroll
@@ -409,90 +419,105 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     const uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
     const int key0 = kb * KB;
 
-    f32x16 sacc[2];
+    // S^T for every query tile; each K fragment read feeds QT MFMAs
+    f32x16 sacc[QT][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
+      for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[u][kt][r] = 0.0f;
 #pragma unroll
       for (int s = 0; s < 5; ++s) {
         const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < QT; ++u)
+          sacc[u][kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[u][s], sacc[u][kt], 0, 0, 0);
       }
     }
     if (key0 + KB > T) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int u = 0; u < QT; ++u)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + key_of_row(32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3)) >= T) sacc[kt][r] = kNegInf;
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key0 + key_of_row(32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3)) >= T) sacc[u][kt][r] = kNegInf;
     }
-    float mx;
-    {
+    float mc[QT];
+#pragma unroll
+    for (int u = 0; u < QT; ++u) {
       float a[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        a[i] = fmaxf(fmaxf(sacc[0][i], sacc[0][i + 8]), fmaxf(sacc[1][i], sacc[1][i + 8]));
-      mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+        a[i] = fmaxf(fmaxf(sacc[u][0][i], sacc[u][0][i + 8]), fmaxf(sacc[u][1][i], sacc[u][1][i + 8]));
+      float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    }
-    // Probabilities are exp(scale (s - m_run)) with a running reference m_run
-    // that only moves when a row maximum exceeds it by more than 2^8 in
-    // exp2 units, so they stay <= 2^8; the final division by the row sum
-    // makes the result independent of the reference.
-    if (__any((mx - m_run) * c > kTau)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      // Probabilities are exp(scale (s - m_run)) with a running reference
+      // m_run that only moves when a row maximum exceeds it by more than 2^8
+      // in exp2 units, so they stay <= 2^8; the final division by the row sum
+      // makes the result independent of the reference.
+      if (__any((mx - m_run[u]) * c > kTau)) {
+        const float m_new = fmaxf(m_run[u], mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * c);
 #pragma unroll
-      for (int dt = 0; dt < 3; ++dt)
+        for (int dt = 0; dt < 3; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      m_run = m_new;
+          for (int r = 0; r < 16; ++r) oacc[u][dt][r] *= alpha;
+        m_run[u] = m_new;
+      }
+      mc[u] = m_run[u] * c;
     }
-    const float mc = m_run * c;
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kt = s >> 1, base = 8 * (s & 1);
-      f16x8 pf;
+      f16x8 pf[QT];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        typedef float f32x2 __attribute__((ext_vector_type(2)));
-        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sacc[kt][base + e], c, -mc)),
-                          __builtin_amdgcn_exp2f(fmaf(sacc[kt][base + e + 1], c, -mc))};
-        const f16x2 ph = __builtin_convertvector(pp, f16x2);
-        pf[e] = ph[0];
-        pf[e + 1] = ph[1];
-      }
+      for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          typedef float f32x2 __attribute__((ext_vector_type(2)));
+          const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sacc[u][kt][base + e], c, -mc[u])),
+                            __builtin_amdgcn_exp2f(fmaf(sacc[u][kt][base + e + 1], c, -mc[u]))};
+          const f16x2 ph = __builtin_convertvector(pp, f16x2);
+          pf[u][e] = ph[0];
+          pf[u][e + 1] = ph[1];
+        }
 #pragma unroll
       for (int dt = 0; dt < 3; ++dt) {  // keys 16s + 8fg + (0..7) of dim row 32dt + fr
         const f16x8 vf = *reinterpret_cast<const f16x8*>(st + voff[s] + dt * 32 * VV_PITCH);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, oacc[dt], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < QT; ++u)
+          oacc[u][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], oacc[u][dt], 0, 0, 0);
       }
     }
   }
 
-  // the row sum sits in O^T row D, register RL of lane group 0
-  const float lsum0 = oacc[2][RL];
-  const float lsum1 = __shfl_xor(lsum0, 32, 64);
-  if (qi >= T) return;
-  const float inv = 1.0f / (fg ? lsum1 : lsum0);
 #pragma unroll
-  for (int dt = 0; dt < 3; ++dt)
+  for (int u = 0; u < QT; ++u) {
+    // the row sum sits in O^T row D, register RL of lane group 0
+    const float lsum0 = oacc[u][2][RL];
+    const float lsum1 = __shfl_xor(lsum0, 32, 64);
+    if (qi[u] >= T) continue;
+    const float inv = 1.0f / (fg ? lsum1 : lsum0);
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      const int d0 = 32 * dt + 8 * qd + 4 * fg;
-      if (d0 >= D) continue;
-      const float a0 = oacc[dt][4 * qd + 0] * inv, a1 = oacc[dt][4 * qd + 1] * inv;
-      const float a2 = oacc[dt][4 * qd + 2] * inv, a3 = oacc[dt][4 * qd + 3] * inv;
-      if constexpr (OUT_FP8) {
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(o) + (img + qi) * ldo + hc + d0) =
-            pack4_e4m3(a0 * out_scale, a1 * out_scale, a2 * out_scale, a3 * out_scale);
-      } else {
-        const f16x4 ov = {(f16)a0, (f16)a1, (f16)a2, (f16)a3};
-        *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(o) + (img + qi) * ldo + hc + d0) = ov;
+    for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int d0 = 32 * dt + 8 * qd + 4 * fg;
+        if (d0 >= D) continue;
+        const float a0 = oacc[u][dt][4 * qd + 0] * inv, a1 = oacc[u][dt][4 * qd + 1] * inv;
+        const float a2 = oacc[u][dt][4 * qd + 2] * inv, a3 = oacc[u][dt][4 * qd + 3] * inv;
+        if constexpr (OUT_FP8) {
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(o) + (img + qi[u]) * ldo + hc + d0) =
+              pack4_e4m3(a0 * out_scale, a1 * out_scale, a2 * out_scale, a3 * out_scale);
+        } else {
+          const f16x4 ov = {(f16)a0, (f16)a1, (f16)a2, (f16)a3};
+          *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(o) + (img + qi[u]) * ldo + hc + d0) = ov;
+        }
       }
-    }
+  }
 }
 
 template <int D>

@@ -150,7 +150,7 @@ struct siglip_model {
   size_t cap_bytes[SIGLIP_STAGE_COUNT] = {};
 
   // per-launch timing: event pairs recorded around launches, resolved on read
-  bool timing = false;
+  uint32_t timing_mask = 0;               // classes whose launches are timed
   std::vector<hipEvent_t> ev_pool;        // 2 events per pending launch
   std::vector<int> ev_class;              // class of each pending pair
   size_t ev_used = 0;                     // pairs in use
@@ -291,8 +291,9 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
 // Brackets one launch with a pair of events when timing is on.
 class LaunchTimer {
  public:
-  LaunchTimer(siglip_model* m, int kclass, hipStream_t s) : m_(m), s_(s) {
-    if (!m_->timing) return;
+  LaunchTimer(siglip_model* m, int kclass, hipStream_t s)
+      : m_(m), s_(s), on_(((m->timing_mask >> kclass) & 1u) != 0) {
+    if (!on_) return;
     if (m_->ev_used * 2 + 2 > m_->ev_pool.size()) {
       for (int i = 0; i < 2; ++i) {
         hipEvent_t e;
@@ -308,12 +309,13 @@ class LaunchTimer {
   ~LaunchTimer() {
     // never throws: a failed record only loses this sample (the launch
     // itself reports its own error)
-    if (m_->timing && hipEventRecord(m_->ev_pool[2 * pair_ + 1], s_) != hipSuccess) m_->timing_lost = true;
+    if (on_ && hipEventRecord(m_->ev_pool[2 * pair_ + 1], s_) != hipSuccess) m_->timing_lost = true;
   }
 
  private:
   siglip_model* m_;
   hipStream_t s_;
+  bool on_;
   size_t pair_ = 0;
 };
 
@@ -777,9 +779,10 @@ SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage, void* ds
   return SIGLIP_OK;
 }
 
-SIGLIP_API int siglip_debug_timing(siglip_model* m, int32_t enable) {
+SIGLIP_API int siglip_debug_timing(siglip_model* m, uint32_t class_mask) {
   if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
-  m->timing = enable != 0;
+  if (class_mask >> SIGLIP_K_COUNT) return fail(SIGLIP_E_INVALID_ARG, "class_mask selects unknown classes");
+  m->timing_mask = class_mask;
   m->ev_used = 0;
   m->timing_lost = false;
   for (int k = 0; k < SIGLIP_K_COUNT; ++k) {
