@@ -84,6 +84,7 @@ struct GemmArgs {
   // output row m = b*vt_tokens + t and column vt_col0 + h*vt_dim + d
   f16* vt; int vt_col0, vt_tokens, vt_heads, vt_dim; int64_t vt_ld;
   float vt_inv_dim;  // 1 / vt_dim
+  int group_m;       // tile-order band height in row blocks (<= 0: N-fastest)
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8,

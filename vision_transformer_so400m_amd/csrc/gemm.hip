@@ -55,15 +55,28 @@ __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3)
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
 
 // Linear workgroup id -> output tile. Workgroups are dispatched round-robin
-// over the 8 XCDs (id % 8), each with its own L2. The remap gives every XCD
-// a contiguous range of tiles, and tiles are numbered N-fastest, so the
-// workgroups that share one row block of A run on the same XCD at about the
-// same time and read that block from HBM once.
-__device__ __forceinline__ void tile_of(int id, int total, int ntn, int* tm, int* tn) {
+// over the 8 XCDs (id % 8), each with its own 4 MB L2. The remap gives every
+// XCD a contiguous range L of tile numbers. Within it, tiles run in bands of
+// gm row blocks: a band is walked column by column (row block fastest), so
+// the workgroups resident on one XCD at a time share a few row blocks of A
+// and a few column blocks of Wt, and both stay in L2 instead of the whole
+// weight matrix streaming past once per row block. gm <= 0 numbers tiles
+// N-fastest over the whole range.
+__device__ __forceinline__ void tile_of(int id, int ntm, int ntn, int gm, int* tm, int* tn) {
+  const int total = ntm * ntn;
   const int total8 = total & ~7;
   const int L = id < total8 ? (id & 7) * (total8 >> 3) + (id >> 3) : id;
-  *tm = L / ntn;
-  *tn = L - *tm * ntn;
+  if (gm <= 0) {
+    *tm = L / ntn;
+    *tn = L - *tm * ntn;
+    return;
+  }
+  const int band = L / (gm * ntn);
+  const int r = L - band * gm * ntn;
+  const int first = band * gm;
+  const int rows = min(gm, ntm - first);  // the last band may be shorter; r < rows * ntn
+  *tn = r / rows;
+  *tm = first + (r - *tn * rows);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.
@@ -95,7 +108,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
   const int ntn = g.N / BN;
   const int ntm = (g.M + BM - 1) / BM;
   int tm, tn;
-  tile_of(blockIdx.x, ntm * ntn, ntn, &tm, &tn);
+  tile_of(blockIdx.x, ntm, ntn, g.group_m, &tm, &tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
   const int nk = (g.K * E) / kRowBytes;

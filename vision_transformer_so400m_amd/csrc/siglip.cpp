@@ -251,6 +251,10 @@ void gemm_qkv(siglip_model* m, const Gemm& g, const void* a, int M, int B, hipSt
   args.vt_dim = m->head_dim;
   args.vt_ld = m->tokens_pad;
   args.vt_inv_dim = 1.0f / (float)m->head_dim;
+  // 3456-wide weight (4 MB e4m3, 8 MB F16) exceeds an XCD's L2 next to the
+  // activations: walk tiles in bands of 8 row blocks (measured ~12% faster
+  // at 46,656 rows than row-block-major order)
+  args.group_m = 8;
   (void)B;
   hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "qkv gemm launch");
 }
