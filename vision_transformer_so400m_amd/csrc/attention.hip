@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = half_swap_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float mc = m_new * c;
     float ls = 0.0f;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(
         sacc[kt][r] = p;
         ls += p;
       }
-    ls += __shfl_xor(ls, 32, 64);
+    ls += half_other(ls);
     if (!__all(m_new == m_run)) {  // some row's maximum moved: rescale the state
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       l_run *= alpha;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
       for (int i = 0; i < 8; ++i)
         a[i] = fmaxf(fmaxf(sacc[u][0][i], sacc[u][0][i + 8]), fmaxf(sacc[u][1][i], sacc[u][1][i + 8]));
       float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = half_swap_max(mx);
       // Probabilities are exp(scale (s - m_run)) with a running reference
       // m_run that only moves when a row maximum exceeds it by more than 2^8
       // in exp2 units, so they stay <= 2^8; the final division by the row sum
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   for (int u = 0; u < QT; ++u) {
     // the row sum sits in O^T row D, register RL of lane group 0
     const float lsum0 = oacc[u][2][RL];
-    const float lsum1 = __shfl_xor(lsum0, 32, 64);
+    const float lsum1 = half_other(lsum0);
     if (qi[u] >= T) continue;
     const float inv = 1.0f / (fg ? lsum1 : lsum0);
 #pragma unroll

@@ -44,6 +44,31 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Exchange with the lane 32 positions away (l <-> l ^ 32) by
+// v_permlane32_swap, no LDS round trip. The second operand is passed through
+// an empty asm so that the compiler sees two distinct values: given the same
+// value twice it folds the two results of the swap into one.
+__device__ __forceinline__ void half_swap(float v, float* lo_half, float* hi_half) {
+  unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+  asm volatile("" : "+v"(b));
+  const auto sw = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  // (elements copied out by value first: a bit cast applied to a vector
+  // element expression reinterprets element 0)
+  const unsigned x0 = sw[0], x1 = sw[1];
+  *lo_half = __builtin_bit_cast(float, x0);  // every lane: value of lane l % 32
+  *hi_half = __builtin_bit_cast(float, x1);  // every lane: value of lane l % 32 + 32
+}
+__device__ __forceinline__ float half_swap_max(float v) {
+  float lo, hi;
+  half_swap(v, &lo, &hi);
+  return fmaxf(lo, hi);
+}
+__device__ __forceinline__ float half_other(float v) {
+  float lo, hi;
+  half_swap(v, &lo, &hi);
+  return __lane_id() < 32 ? hi : lo;
+}
+
 // GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). Since
 // 0.5 (1 + tanh(z)) = 1 / (1 + exp(-2z)), this is x / (1 + exp(-2z)) with
 // z = sqrt(2/pi) x (1 + 0.044715 x^2): one exp2 and one reciprocal (both
