@@ -92,6 +92,89 @@ def cpu_baseline(wt, pixels, heads):
                       f"(unquantized), {dt:.2f} s wall"}
 
 
+def time_calls(model, x, out, steps, warmup=3):
+    import torch
+    for _ in range(warmup):
+        model.encode(x, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        model.encode(x, out=out)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def class_times(model, x, out, calls=2):
+    """Mean HIP-event time per launch (us) and launches per call, per kernel class."""
+    import torch
+    import vision_transformer_so400m_amd as V
+    model.debug_timing(True)
+    for _ in range(calls):
+        model.encode(x, out=out)
+    torch.cuda.synchronize()
+    res = {}
+    for k in V.KERNEL_CLASSES:
+        ms, n = model.debug_timing_read(k)
+        if n:
+            res[k] = (ms * 1e3 / n, n // calls)
+    model.debug_timing(False)
+    return res
+
+
+def sweep(args):
+    """Batch sweep and per-block times of the 27-layer model (one JSON line):
+    images/s at B = 1..64 for e4m3 and F16 GEMM operands; the projected-
+    attention block (LN + QKV + attention + out-proj) and the MLP block
+    (LN + up + down) from per-launch HIP events at B = 1 and B = 64; fused
+    against separate Q/K/V projections."""
+    import torch
+
+    import synthetic as S
+    import vision_transformer_so400m_amd as V
+
+    d = S.SO400M
+    wt = S.make_weights(d, 2)
+    blob = S.pack_blob(d, wt)
+    del wt
+    xall = torch.from_numpy(S.make_pixels(d, 64, 2)).cuda()
+    res = {"workload": "SigLIP So400m/14 27 layers + MAP, synthetic seed-2 input and weights", "batches": {}, "blocks": {},
+           "qkv_projections": {}}
+    batches = [1, 2, 4, 8, 16, 32, 64]
+    for fp8 in (True, False):
+        tag = "e4m3" if fp8 else "f16"
+        model = V.Model(blob, max_batch=64, fp8=fp8)
+        res["batches"][tag] = {}
+        for b in batches:
+            x = xall[:b].contiguous()
+            out = torch.empty((b, 1, d.width), dtype=torch.float16, device="cuda")
+            ms = time_calls(model, x, out, args.sweep_steps if b > 1 else 4 * args.sweep_steps)
+            res["batches"][tag][str(b)] = {"ms": round(ms, 4), "images_per_s": round(b / ms * 1e3, 2)}
+            if b in (1, 64):
+                ct = class_times(model, x, out)
+                ln = ct["LAYERNORM"][0]
+                blocks = {
+                    "projected_attention_us": round(ln + ct["QKV"][0] + ct["ATTENTION"][0] + ct["OUT_PROJ"][0], 2),
+                    "mlp_block_us": round(ln + ct["MLP_UP"][0] + ct["MLP_DOWN"][0], 2),
+                    "per_launch_us": {k: round(v[0], 2) for k, v in ct.items()},
+                }
+                res["blocks"][f"{tag}_b{b}"] = blocks
+        model.close()
+    for sep in (False, True):
+        model = V.Model(blob, max_batch=64, fp8=True, separate_qkv=sep)
+        tag = "separate" if sep else "fused"
+        res["qkv_projections"][tag] = {}
+        for b in (1, 64):
+            x = xall[:b].contiguous()
+            out = torch.empty((b, 1, d.width), dtype=torch.float16, device="cuda")
+            ms = time_calls(model, x, out, args.sweep_steps if b > 1 else 4 * args.sweep_steps)
+            ct = class_times(model, x, out)
+            qkv_us = ct["QKV"][0] * ct["QKV"][1] / d.depth  # all launches of the class, per layer
+            res["qkv_projections"][tag][f"b{b}"] = {"ms": round(ms, 4), "qkv_us_per_layer": round(qkv_us, 2),
+                                                    "map_kv_us": round(ct["MAP_KV"][0] * ct["MAP_KV"][1], 2)}
+        model.close()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,12 +184,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 512 MiB device copy (HBM-counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: batch sweep, per-block times, fused vs separate QKV")
+    ap.add_argument("--sweep-steps", type=int, default=10)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build runs the encoder on a single MI355X "
               "(data-parallel sharding is described, not built). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args)
+        return
 
     import numpy as np
     import torch

@@ -59,6 +59,13 @@ typedef struct {
    * operand x is stored as e4m3(x * 2^-exp), saturating at +-448, and each
    * product is rescaled by 2^(2*exp). Ignored for F16. Range -8..8. */
   int32_t fp8_scale_exp;
+  /* 0 = one fused Q/K/V projection per layer and one fused MAP K/V
+   * projection (the default); 1 = separate projections of width columns
+   * each (three per layer, two in the MAP head). Page "Single-layer SigLIP
+   * vision benchmark", "Fused encoder QKV and MAP KV", compares the two
+   * forms. Each output element is computed with the same operands and the
+   * same summation order either way, so the results are identical. */
+  int32_t separate_qkv;
 } siglip_options;
 
 /*

@@ -106,6 +106,25 @@ def test_bad_options(blob1, kw, msg):
     assert e.status == V.SIGLIP_E_INVALID_ARG and msg in e.message
 
 
+def test_options_struct_matches_header():
+    """The binding's siglip_options has the header's fields, in order."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} siglip_options;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"int32_t\s+(\w+)\s*;", body)
+    assert fields == [f[0] for f in V.siglip_options._fields_]
+    assert all(f[1] is ctypes.c_int32 for f in V.siglip_options._fields_)
+
+
+def test_bad_separate_qkv_value(blob1):
+    lib = V.load_library()
+    out = ctypes.c_void_p()
+    opt = V.siglip_options(0, 1, 0, -4, 2)
+    st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
+    assert st == V.SIGLIP_E_INVALID_ARG and not out.value
+    assert b"separate_qkv" in lib.siglip_last_error()
+
+
 def test_unsupported_width_is_reported_before_the_device():
     d = S.small_dims(1)   # width 144: not a multiple of 128
     e = _create(bytes(S.pack_blob(d, S.make_weights(d, 0))))

@@ -385,6 +385,34 @@ def test_determinism_and_nan_poisoned_workspace(V):
     assert np.isfinite(a).all()
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
+def test_separate_qkv_matches_fused_bitwise(V, fp8):
+    """Separate Q/K/V (and MAP K/V) projections against the fused ones: every
+    output element has the same operands and summation order, so results are
+    identical, at batch 2 (small tiles) and batch 64 (the large-batch tile
+    shapes, where the fused and separate widths take different tiles)."""
+    dims = S.SO400M.with_depth(2)
+    wt = S.make_weights(dims, 3)
+    blob = S.pack_blob(dims, wt)
+    del wt
+    for b in (2, 64):
+        _flush(f"separate vs fused QKV, fp8={fp8}, B={b}")
+        x = torch.from_numpy(S.make_pixels(dims, b, 3)).cuda()
+        fused = V.Model(blob, max_batch=b, fp8=fp8)
+        sep = V.Model(blob, max_batch=b, fp8=fp8, separate_qkv=True)
+        fused.debug_capture(1)
+        sep.debug_capture(1)
+        yf = fused.encode(x)
+        ys = sep.encode(x)
+        torch.cuda.synchronize()
+        assert np.isfinite(yf.cpu().numpy()).all()
+        np.testing.assert_array_equal(ys.cpu().numpy().view(np.uint16), yf.cpu().numpy().view(np.uint16))
+        for st in ("QKV", "V_T", "MAP_KV"):
+            np.testing.assert_array_equal(sep.debug_stage(st).view(np.uint8), fused.debug_stage(st).view(np.uint8))
+        fused.close()
+        sep.close()
+
+
 def test_four_token_full_width_diagnostic(V):
     dims = S.four_token_dims(2)
     _flush("four-token diagnostic")

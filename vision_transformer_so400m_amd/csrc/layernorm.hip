@@ -18,11 +18,14 @@ namespace {
 
 constexpr int kMaxChunks = 4;  // 16-byte chunks per lane: width <= 64 * 8 * 4 = 2048
 
-template <bool OUT_FP8>
+// WIDTH > 0 fixes the row width at compile time (the chunk bounds then fold
+// into the unrolled loops); WIDTH = 0 takes it from the argument.
+template <bool OUT_FP8, int WIDTH>
 __global__ __launch_bounds__(256) void layernorm_kernel(
     const f16* __restrict__ x, int64_t ldx, void* __restrict__ y, int64_t ldy,
     const float* __restrict__ gamma, const float* __restrict__ beta, int rows,
-    int width, float eps, float out_scale) {
+    int width_arg, float eps, float out_scale) {
+  const int width = WIDTH > 0 ? WIDTH : width_arg;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -96,10 +99,16 @@ hipError_t launch_layernorm(const f16* x, int64_t ldx, void* y, int64_t ldy,
       (ldx & 7) || (ldy & 7))
     return hipErrorInvalidValue;
   dim3 grid((rows + 3) / 4);
-  if (out_fp8)
-    hipLaunchKernelGGL(layernorm_kernel<true>, grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
-  else
-    hipLaunchKernelGGL(layernorm_kernel<false>, grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
+  if (width == 1152) {  // the So400m width
+    if (out_fp8)
+      hipLaunchKernelGGL((layernorm_kernel<true, 1152>), grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
+    else
+      hipLaunchKernelGGL((layernorm_kernel<false, 1152>), grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
+  } else if (out_fp8) {
+    hipLaunchKernelGGL((layernorm_kernel<true, 0>), grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
+  } else {
+    hipLaunchKernelGGL((layernorm_kernel<false, 0>), grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
+  }
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct Gemm {
 struct Layer {
   float *ln1_g, *ln1_b, *ln2_g, *ln2_b;
   Gemm qkv, out, mlp1, mlp2;
+  Gemm q, k, v;  // the three column blocks of qkv (separate-projection option only)
 };
 
 struct BlobHeader {
@@ -124,6 +125,8 @@ struct siglip_model {
   std::vector<Layer> L;
   float *lnf_g = nullptr, *lnf_b = nullptr;
   Gemm mq, mkv, mout, mmlp1, mmlp2;
+  Gemm mk, mv;  // the two column blocks of mkv (separate-projection option only)
+  bool separate_qkv = false;
   float *mln_g = nullptr, *mln_b = nullptr;
   f16* map_q = nullptr;  // [width]
 
@@ -201,6 +204,23 @@ Gemm make_gemm(siglip_model* m, const TensorRef& w, const TensorRef& b, float* s
   return g;
 }
 
+// Columns c0 .. c0+n-1 of a host [rows, cols] tensor (a weight [in, out] or
+// a bias [1, out]) as a contiguous copy in buf.
+TensorRef column_block(const TensorRef& t, int64_t c0, int64_t n, std::vector<float>& buf) {
+  buf.resize((size_t)(t.rows * n));
+  for (int64_t r = 0; r < t.rows; ++r)
+    std::memcpy(buf.data() + r * n, t.host + r * t.cols + c0, (size_t)n * 4);
+  return TensorRef{buf.data(), t.rows, n};
+}
+
+// make_gemm of columns c0 .. c0+n-1 of a fused projection
+Gemm make_gemm_block(siglip_model* m, const TensorRef& w, const TensorRef& b, int64_t c0, int64_t n, float* staging) {
+  std::vector<float> wb, bb;
+  const TensorRef ws = column_block(w, c0, n, wb);
+  const TensorRef bs = column_block(b, c0, n, bb);
+  return make_gemm(m, ws, bs, staging);
+}
+
 void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, void* c, int64_t ldc, int epi,
           bool out_fp8, const f16* res, int64_t ldres, hipStream_t s) {
   GemmArgs args{};
@@ -226,7 +246,41 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
 
 // The fused QKV projection: Q and K row-major into qkv, V transposed per
 // head into vt when the streaming attention is used.
-void gemm_qkv(siglip_model* m, const Gemm& g, const void* a, int M, int B, hipStream_t s) {
+void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hipStream_t s) {
+  const Gemm& g = Ly.qkv;
+  if (m->separate_qkv) {
+    // Q and K into their columns of the fused row; V as its own projection,
+    // transposed per head (all its columns are V: vt_col0 = 0)
+    const int W = m->width;
+    gemm(m, Ly.q, a, W, M, m->qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    gemm(m, Ly.k, a, W, M, m->qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    if (!m->vt_path) {
+      gemm(m, Ly.v, a, W, M, m->qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      return;
+    }
+    GemmArgs args{};
+    args.a = a;
+    args.lda = W;
+    args.w = Ly.v.w;
+    args.ldw = Ly.v.k_pad;
+    args.c = m->qkv + 2 * W;  // not written: every column goes to vt
+    args.ldc = 3 * W;
+    args.bias = Ly.v.bias;
+    args.M = M;
+    args.N = Ly.v.n_pad;
+    args.K = Ly.v.k_pad;
+    args.acc_scale = m->acc_scale;
+    args.out_scale = m->op_scale;
+    args.vt = m->vt;
+    args.vt_col0 = 0;
+    args.vt_tokens = m->tokens;
+    args.vt_heads = m->heads;
+    args.vt_dim = m->head_dim;
+    args.vt_ld = m->tokens_pad;
+    args.vt_inv_dim = 1.0f / (float)m->head_dim;
+    hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "v gemm launch");
+    return;
+  }
   if (!m->vt_path) {
     gemm(m, g, a, m->width, M, m->qkv, 3 * m->width, EPI_BIAS, false, nullptr, 0, s);
     return;
@@ -364,7 +418,7 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     if (ci) capture(m, SIGLIP_STAGE_LN1, m->a, cb(SIGLIP_STAGE_LN1), s);
     {
       LaunchTimer lt(m, SIGLIP_K_QKV, s);
-      gemm_qkv(m, Ly.qkv, m->a, M, B, s);
+      gemm_qkv(m, Ly, m->a, M, B, s);
     }
     if (ci) capture(m, SIGLIP_STAGE_QKV, m->qkv, cb(SIGLIP_STAGE_QKV), s);
     if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, m->vt, cb(SIGLIP_STAGE_V_T), s);
@@ -410,7 +464,12 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
   f16* kv = m->qkv;  // [M, 2W]
   {
     LaunchTimer lt(m, SIGLIP_K_MAP_KV, s);
-    gemm(m, m->mkv, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+    if (m->separate_qkv) {
+      gemm(m, m->mk, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, m->mv, m->a, W, M, kv + W, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+    } else {
+      gemm(m, m->mkv, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+    }
   }
   if (cap) capture(m, SIGLIP_STAGE_MAP_KV, kv, cb(SIGLIP_STAGE_MAP_KV), s);
   {
@@ -482,6 +541,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_INVALID_ARG, "gemm_precision must be 0 (F16) or 1 (FP8)");
   if (opt->gemm_precision == 1 && (opt->fp8_scale_exp < -8 || opt->fp8_scale_exp > 8))
     return fail(SIGLIP_E_INVALID_ARG, "fp8_scale_exp must be in -8..8");
+  if (opt->separate_qkv != 0 && opt->separate_qkv != 1)
+    return fail(SIGLIP_E_INVALID_ARG, "separate_qkv must be 0 or 1");
   if (blob_bytes < sizeof(BlobHeader)) return fail(SIGLIP_E_BAD_BLOB, "blob shorter than its 64-byte header");
   BlobHeader h;
   std::memcpy(&h, blob, sizeof h);
@@ -572,6 +633,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->mlp_pad = (int)round_up(F, kNAlign);  // U is both an N (MLP up) and a K (MLP down) dimension
     m->vt_path = flash_attention_vt_supported(m->head_dim);
     m->tokens_pad = (int)round_up(T, 64);
+    m->separate_qkv = opt->separate_qkv == 1;
 
     const size_t staging_floats = (size_t)std::max<int64_t>({(int64_t)P * W, 3LL * W * W, (int64_t)W * F, (int64_t)T * W});
     float* staging = static_cast<float*>(m->dalloc(staging_floats * 4));
@@ -585,7 +647,13 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
       Ly.ln1_b = upload_f32(m, r.ln1b);
       Ly.ln2_g = upload_f32(m, r.ln2g);
       Ly.ln2_b = upload_f32(m, r.ln2b);
-      Ly.qkv = make_gemm(m, r.qkvw, r.qkvb, staging);
+      if (m->separate_qkv) {
+        Ly.q = make_gemm_block(m, r.qkvw, r.qkvb, 0, W, staging);
+        Ly.k = make_gemm_block(m, r.qkvw, r.qkvb, W, W, staging);
+        Ly.v = make_gemm_block(m, r.qkvw, r.qkvb, 2 * W, W, staging);
+      } else {
+        Ly.qkv = make_gemm(m, r.qkvw, r.qkvb, staging);
+      }
       Ly.out = make_gemm(m, r.outw, r.outb, staging);
       Ly.mlp1 = make_gemm(m, r.m1w, r.m1b, staging);
       Ly.mlp2 = make_gemm(m, r.m2w, r.m2b, staging);
@@ -594,7 +662,12 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->lnf_g = upload_f32(m, lfg);
     m->lnf_b = upload_f32(m, lfb);
     m->mq = make_gemm(m, qw, qb, staging);
-    m->mkv = make_gemm(m, kvw, kvb, staging);
+    if (m->separate_qkv) {
+      m->mk = make_gemm_block(m, kvw, kvb, 0, W, staging);
+      m->mv = make_gemm_block(m, kvw, kvb, W, W, staging);
+    } else {
+      m->mkv = make_gemm(m, kvw, kvb, staging);
+    }
     m->mout = make_gemm(m, ow, ob, staging);
     m->mmlp1 = make_gemm(m, m1w, m1b, staging);
     m->mmlp2 = make_gemm(m, m2w, m2b, staging);
