@@ -66,6 +66,16 @@ typedef struct {
    * forms. Each output element is computed with the same operands and the
    * same summation order either way, so the results are identical. */
   int32_t separate_qkv;
+  /* 0 = MAP head with its K/V projection folded away (the default where
+   * supported: heads <= 16, width a multiple of 64, tokens <= 1024): the
+   * probe's scores are Z . (W_k,h q_h) and each head's output is
+   * (sum_t p_t Z_t) W_v,h + b_v,h, the same real numbers as projecting every
+   * token (page "Single-layer SigLIP vision benchmark", intro: one fused K/V
+   * projection and one shared probe), computed from the F16 final-LN
+   * output with F32 accumulation in both precision modes.
+   * 1 = the explicit K/V projection of every token (an e4m3 GEMM in FP8
+   * mode) followed by the probe attention. */
+  int32_t map_explicit_kv;
 } siglip_options;
 
 /*
@@ -173,8 +183,10 @@ typedef enum {
   SIGLIP_STAGE_LN2 = 5,        /* [M, width]   F16 | e4m3 code                */
   SIGLIP_STAGE_MLP_HIDDEN = 6, /* [M, mlp_pad] F16 | e4m3 code (post-GELU)    */
   SIGLIP_STAGE_H_OUT = 7,      /* [M, width]   F16  after MLP residual        */
-  SIGLIP_STAGE_FINAL_LN = 8,   /* [M, width]   F16 | e4m3 code                */
-  SIGLIP_STAGE_MAP_KV = 9,     /* [M, 2*width] F16                            */
+  SIGLIP_STAGE_FINAL_LN = 8,   /* [M, width]   F16 | e4m3 code (F16 whenever
+                                  the MAP K/V projection is folded)           */
+  SIGLIP_STAGE_MAP_KV = 9,     /* [M, 2*width] F16 (explicit MAP K/V only;
+                                  0 rows when folded)                         */
   SIGLIP_STAGE_MAP_ATTN = 10,  /* [B, width]   F16 | e4m3 code                */
   SIGLIP_STAGE_MAP_Y = 11,     /* [B, width]   F16  MAP output projection     */
   SIGLIP_STAGE_MAP_LN = 12,    /* [B, width]   F16 | e4m3 code                */

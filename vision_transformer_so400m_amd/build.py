@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libsiglip.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["gemm.hip", "layernorm.hip", "attention.hip", "convert.hip", "siglip.cpp"]
+SOURCES = ["gemm.hip", "layernorm.hip", "attention.hip", "map.hip", "convert.hip", "siglip.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

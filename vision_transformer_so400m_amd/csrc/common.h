@@ -144,6 +144,18 @@ hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv,
                                 float scale, bool out_fp8, float out_scale,
                                 hipStream_t s);
 
+// MAP head with the K/V projection folded (map.hip). phase 0: scores
+// [batch, 16, tokens] F32 = (Z . u_h) * scale * log2(e); phase 1: softmax per
+// (image, head), zbar [batch, 16, width] F32 = sum_t p_t Z_t, then
+// o[b, h*head_dim + d] = zbar_h . W_v[:, h*head_dim + d] + bv (F16, or e4m3
+// codes of o*out_scale). u_hi/u_lo: [16, width] F16, rows >= heads zero;
+// wvt: W_v transposed, wvt[(h*head_dim + d) * width + k] = W_v[k][h*head_dim + d].
+bool map_fold_supported(int width, int heads, int head_dim, int tokens);
+hipError_t launch_map_fold(const f16* z, int64_t ldz, const f16* u_hi, const f16* u_lo, const float* wvt,
+                           const float* bv, float* scores, float* zbar, int batch, int tokens, int heads,
+                           int head_dim, int width, float scale, bool out_fp8, float out_scale, void* o,
+                           int64_t ldo, hipStream_t s, int phase);
+
 // ------------------------------------------------------------ conversion
 // F16 [rows, cols] (row stride ldx) -> [rows, cols_pad] F16 or e4m3 codes of
 // x*scale, columns cols..cols_pad-1 set to zero.

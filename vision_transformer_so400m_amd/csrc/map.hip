@@ -1,0 +1,290 @@
+// MAP head probe attention with the K/V projection folded away.
+//
+// The MAP head ([SLB] intro and mermaid figure: one learned probe, its query
+// projection, one fused K/V projection of the final-LN tokens Z, softmax
+// attention per head, output projection) needs, per image b and head h,
+//   scores_t = q_h . K_{t,h} = Z_t . (W_k,h q_h) + b_k,h . q_h
+//   o_h      = sum_t p_t V_{t,h} = (sum_t p_t Z_t) W_v,h + b_v,h
+// (p sums to one). The probe is shared by every image ([SLB]: each batch uses
+// the same learned probe), so u_h = W_k,h q_h is computed once at create, and
+// the constant b_k,h . q_h cancels in the softmax. That replaces the
+// [M, width] x [width, 2 width] K/V GEMM (3.9 GFLOP per image) by one pass
+// over Z for the scores, one for the probability-weighted sum of Z, and a
+// per-head [width] x [width, head_dim] product: the same real numbers, about
+// 70x fewer operations, and no e4m3 rounding of K and V.
+//
+//  * map_scores: S[b][h][t] = (Z[b T + t,:] . u_h) * scale * log2(e), F32, by
+//    v_mfma_f32_16x16x32_f16 on 16-token x 16-head tiles. u is held as two
+//    F16 parts (u = hi + lo), so the scores carry F32-level accuracy.
+//  * map_pool: per image and 64-column block, the softmax over the tokens
+//    (max, exp2, sum in F32, probabilities in LDS) and zbar_h = sum_t p_t Z_t.
+//  * map_vproj: o[b, h*D + d] = zbar_h . W_v[:, h*D + d] + b_v, written as the
+//    operand type of the MAP output projection (F16 or e4m3 codes).
+#include "common.h"
+
+#include <algorithm>
+
+namespace siglip {
+namespace {
+
+constexpr int kMapHeads = 16;  // head slots of a score row (heads beyond H are zero)
+
+// A 16 x 16 tile of scores (tokens t0..t0+15 on the MFMA rows, head slots on
+// the columns) per workgroup: wave w sums the width/4 columns
+// [w width/4, (w+1) width/4) in K steps of 32, lane (i, g) = (lane % 16,
+// lane / 16) loading Z[t0+i][k0 + 8g .. +7] and the same columns of u for
+// head slot i; the four partial tiles are added in LDS.
+__global__ __launch_bounds__(256) void map_scores_kernel(const f16* __restrict__ z, int64_t ldz,
+                                                         const f16* __restrict__ u_hi,
+                                                         const f16* __restrict__ u_lo, int width,
+                                                         float* __restrict__ s, int rows, int T, float sl2) {
+  __shared__ f32x4 part[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int i = lane & 15;
+  const int g = lane >> 4;
+  const int t0 = blockIdx.x * 16;
+  const int row = min(t0 + i, rows - 1);  // rows past the end re-read the last row; never stored
+  const int quarter = width >> 2;
+  const int kb = wave * quarter + 8 * g;
+  const f16* zr = z + (int64_t)row * ldz + kb;
+  const f16* uh = u_hi + (int64_t)i * width + kb;
+  const f16* ul = u_lo + (int64_t)i * width + kb;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 9
+  for (int k0 = 0; k0 < quarter; k0 += 32) {
+    const f16x8 a = *reinterpret_cast<const f16x8*>(zr + k0);
+    const f16x8 h = *reinterpret_cast<const f16x8*>(uh + k0);
+    const f16x8 l = *reinterpret_cast<const f16x8*>(ul + k0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, l, acc, 0, 0, 0);
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    const f32x4 sum = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    // lane holds rows t0 + 4g + r (r = 0..3) of head slot i; scores are
+    // stored per image and head: s[(b * 16 + i) * T + t] for row b * T + t
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = t0 + 4 * g + r;
+      if (m < rows) {
+        const int b = m / T;
+        s[((int64_t)b * kMapHeads + i) * T + (m - b * T)] = sum[r] * sl2;
+      }
+    }
+  }
+}
+
+// Sum of v over the four 16-lane rows of a wave, in every lane
+// (v_permlane16_swap / v_permlane32_swap exchanges; second operands made
+// opaque so the compiler keeps the two results of each swap apart).
+__device__ __forceinline__ float row4_sum(float v) {
+  unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+  asm volatile("" : "+v"(b));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  const unsigned x0 = s16[0], x1 = s16[1];
+  v = __builtin_bit_cast(float, x0) + __builtin_bit_cast(float, x1);  // rows (0+1, 0+1, 2+3, 2+3)
+  a = __builtin_bit_cast(unsigned, v);
+  b = a;
+  asm volatile("" : "+v"(b));
+  const auto s32 = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  const unsigned y0 = s32[0], y1 = s32[1];
+  return __builtin_bit_cast(float, y0) + __builtin_bit_cast(float, y1);
+}
+
+// One workgroup of 512 threads (8 waves) per (64-column block, image).
+// First each wave takes two heads: softmax statistics over the tokens (max,
+// then exp2 and sum in F32), probabilities to LDS as [token][16]. Then thread
+// (c, q) = (tid / 16, tid % 16) takes the tokens t = c (mod 32) and
+// columns c0 + 4q .. +3 for all 16 head slots (64 accumulators): one 8-byte
+// load of Z per token. The four token slices of a wave are summed by lane
+// exchanges, the 8 waves through LDS.
+constexpr int kPoolThreads = 512;
+constexpr int kPoolWaves = kPoolThreads / 64;
+constexpr int kPoolSlices = kPoolThreads / 16;
+
+__global__ __launch_bounds__(kPoolThreads) void map_pool_kernel(const f16* __restrict__ z, int64_t ldz,
+                                                        const float* __restrict__ s, int T, int heads,
+                                                        float* __restrict__ zbar, int width) {
+  extern __shared__ float p[];  // [T][kMapHeads]; reused for the wave partials [waves][16][64]
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  __shared__ float inv_l[kMapHeads];
+  for (int h = tid >> 6; h < kMapHeads; h += kPoolWaves) {
+    const int lane = tid & 63;
+    const float* sh = s + ((int64_t)b * kMapHeads + h) * T;  // this image's scores of head h
+    float m = -__builtin_inff();
+    for (int t = lane; t < T; t += 64) m = fmaxf(m, sh[t]);
+    m = wave_max(m);
+    float l = 0.f;
+    for (int t = lane; t < T; t += 64) {
+      const float e = __builtin_amdgcn_exp2f(sh[t] - m);
+      p[t * kMapHeads + h] = e;
+      l += e;
+    }
+    l = wave_sum(l);
+    if (lane == 0) inv_l[h] = 1.0f / l;
+  }
+  __syncthreads();
+
+  const int c = tid >> 4;
+  const int q = tid & 15;
+  const int col = blockIdx.x * 64 + 4 * q;
+  const f16* zc = z + (int64_t)b * T * ldz + col;
+  float acc[kMapHeads][4];
+#pragma unroll
+  for (int h = 0; h < kMapHeads; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
+  constexpr int kRound = 8;  // tokens whose loads are in flight together
+  for (int t0 = c; t0 < T; t0 += kRound * kPoolSlices) {
+    f16x4 zv[kRound];
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int t = t0 + kPoolSlices * j;
+      zv[j] = t < T ? *reinterpret_cast<const f16x4*>(zc + (int64_t)t * ldz) : f16x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int t = t0 + kPoolSlices * j;
+      if (t >= T) break;
+      const f32x4* pt = reinterpret_cast<const f32x4*>(p + t * kMapHeads);
+      float zf[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zf[e] = (float)zv[j][e];
+#pragma unroll
+      for (int h4 = 0; h4 < kMapHeads / 4; ++h4) {
+        const f32x4 pv = pt[h4];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[4 * h4 + hh][e] = fmaf(pv[hh], zf[e], acc[4 * h4 + hh][e]);
+      }
+    }
+  }
+  // lanes q, q+16, q+32, q+48 of a wave hold the four token slices of column quad q
+#pragma unroll
+  for (int h = 0; h < kMapHeads; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[h][e] = row4_sum(acc[h][e]);
+  __syncthreads();  // every thread is done reading p: reuse it for the wave partials
+  const int wave = tid >> 6, lane = tid & 63;
+  f32x4* part = reinterpret_cast<f32x4*>(p);  // [waves][16 heads][16 quads]
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < kMapHeads; ++h)
+      part[(wave * kMapHeads + h) * 16 + lane] = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+  }
+  __syncthreads();
+  if (tid < kMapHeads * 16) {
+    const int h = tid >> 4, qq = tid & 15;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kPoolWaves; ++w) sum += part[(w * kMapHeads + h) * 16 + qq];
+    if (h < heads) {
+      const float inv = inv_l[h];
+      *reinterpret_cast<f32x4*>(zbar + ((int64_t)b * kMapHeads + h) * width + blockIdx.x * 64 + 4 * qq) =
+          f32x4{sum[0] * inv, sum[1] * inv, sum[2] * inv, sum[3] * inv};
+    }
+  }
+}
+
+// One workgroup per (head, group of 4 images). wvt holds W_v transposed per
+// head: wvt[(h*D + d) * width + k] = W_v[k][h*D + d]. Thread (kc, d) =
+// (tid / D, tid % D) sums the K chunk [kc width/8, (kc+1) width/8) for the
+// 4 images (zbar rows staged in LDS); the 8 chunks are added in LDS.
+constexpr int kVprojImages = 4;
+constexpr int kVprojChunks = 8;
+
+template <bool OUT_FP8>
+__global__ __launch_bounds__(1024) void map_vproj_kernel(const float* __restrict__ zbar, const float* __restrict__ wvt,
+                                                         const float* __restrict__ bv, int width, int D, int batch,
+                                                         void* __restrict__ o, int64_t ldo, float out_scale) {
+  extern __shared__ float sm[];  // zbar rows [kVprojImages][width], then partials [kVprojChunks][kVprojImages][D]
+  const int h = blockIdx.x;
+  const int b0 = blockIdx.y * kVprojImages;
+  const int nb = min(kVprojImages, batch - b0);
+  for (int i = threadIdx.x; i < kVprojImages * width; i += blockDim.x) {
+    const int bi = i / width;
+    sm[i] = bi < nb ? zbar[((int64_t)(b0 + bi) * kMapHeads + h) * width + (i - bi * width)] : 0.f;
+  }
+  __syncthreads();
+  const int kc = threadIdx.x / D;
+  const int d = threadIdx.x - kc * D;
+  const int chunk = width / kVprojChunks;
+  float acc[kVprojImages] = {0.f, 0.f, 0.f, 0.f};
+  if (kc < kVprojChunks) {
+    const float* wr = wvt + (int64_t)(h * D + d) * width + kc * chunk;
+    const float* zr = sm + kc * chunk;
+#pragma unroll 4
+    for (int k = 0; k < chunk; k += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(wr + k);
+#pragma unroll
+      for (int bi = 0; bi < kVprojImages; ++bi) {
+        const f32x4 zv = *reinterpret_cast<const f32x4*>(zr + bi * width + k);
+        acc[bi] = fmaf(w[0], zv[0], fmaf(w[1], zv[1], fmaf(w[2], zv[2], fmaf(w[3], zv[3], acc[bi]))));
+      }
+    }
+  }
+  float* red = sm + kVprojImages * width;
+  if (kc < kVprojChunks)
+#pragma unroll
+    for (int bi = 0; bi < kVprojImages; ++bi) red[(kc * kVprojImages + bi) * D + d] = acc[bi];
+  __syncthreads();
+  if (threadIdx.x < kVprojImages * D) {
+    const int bi = threadIdx.x / D, dd = threadIdx.x - bi * D;
+    if (bi < nb) {
+      float v = bv[h * D + dd];
+#pragma unroll
+      for (int c = 0; c < kVprojChunks; ++c) v += red[(c * kVprojImages + bi) * D + dd];
+      const int64_t at = (int64_t)(b0 + bi) * ldo + h * D + dd;
+      if constexpr (OUT_FP8)
+        reinterpret_cast<uint8_t*>(o)[at] = (uint8_t)(cvt_pk_e4m3(v * out_scale, 0.f, 0u, false) & 0xFF);
+      else
+        reinterpret_cast<f16*>(o)[at] = (f16)v;
+    }
+  }
+}
+
+}  // namespace
+
+bool map_fold_supported(int width, int heads, int head_dim, int tokens) {
+  return heads >= 1 && heads <= kMapHeads && width % 128 == 0 && width <= 4096 && tokens >= 1 &&
+         tokens <= 1024 && head_dim >= 4 && head_dim % 4 == 0 && head_dim * kVprojChunks <= 1024 &&
+         heads * head_dim == width;
+}
+
+hipError_t launch_map_fold(const f16* z, int64_t ldz, const f16* u_hi, const f16* u_lo, const float* wvt,
+                           const float* bv, float* scores, float* zbar, int batch, int tokens, int heads,
+                           int head_dim, int width, float scale, bool out_fp8, float out_scale, void* o,
+                           int64_t ldo, hipStream_t s, int phase) {
+  if (!map_fold_supported(width, heads, head_dim, tokens) || batch < 1 || batch > 65535 || ldz < width ||
+      (ldz & 7) || ldo < width)
+    return hipErrorInvalidValue;
+  const int rows = batch * tokens;
+  if (phase == 0) {
+    const float sl2 = scale * 1.4426950408889634f;
+    hipLaunchKernelGGL(map_scores_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, z, ldz, u_hi, u_lo,
+                       width, scores, rows, tokens, sl2);
+    return hipGetLastError();
+  }
+  // probabilities [tokens][16] F32, reused for waves x 16 x 16 partial sums of 16 bytes
+  const size_t pool_lds = std::max<size_t>((size_t)kMapHeads * tokens * sizeof(float), kPoolWaves * kMapHeads * 16 * 16);
+  hipLaunchKernelGGL(map_pool_kernel, dim3((unsigned)(width / 64), (unsigned)batch), dim3(kPoolThreads), pool_lds, s, z, ldz,
+                     scores, tokens, heads, zbar, width);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)heads, (unsigned)((batch + kVprojImages - 1) / kVprojImages));
+  const dim3 block((unsigned)(head_dim * kVprojChunks));
+  const size_t lds = ((size_t)kVprojImages * width + (size_t)kVprojChunks * kVprojImages * head_dim) * sizeof(float);
+  if (out_fp8)
+    hipLaunchKernelGGL(map_vproj_kernel<true>, grid, block, lds, s, zbar, wvt, bv, width, head_dim, batch, o, ldo,
+                       out_scale);
+  else
+    hipLaunchKernelGGL(map_vproj_kernel<false>, grid, block, lds, s, zbar, wvt, bv, width, head_dim, batch, o, ldo,
+                       out_scale);
+  return hipGetLastError();
+}
+
+}  // namespace siglip

@@ -127,6 +127,11 @@ struct siglip_model {
   Gemm mq, mkv, mout, mmlp1, mmlp2;
   Gemm mk, mv;  // the two column blocks of mkv (separate-projection option only)
   bool separate_qkv = false;
+  // MAP head with the K/V projection folded: u_h = W_k,h q_h in two F16
+  // parts, W_v transposed per head [width (h, d), width (k)] and b_v F32
+  bool map_fold = false;
+  f16 *u_hi = nullptr, *u_lo = nullptr;
+  float *wv = nullptr, *bv = nullptr;
   float *mln_g = nullptr, *mln_b = nullptr;
   f16* map_q = nullptr;  // [width]
 
@@ -144,6 +149,8 @@ struct siglip_model {
   void* ma = nullptr;   // [B, width] operand type
   void* mu = nullptr;   // [B, mlp_pad] operand type
   f16* vt = nullptr;    // [B*heads*head_dim, tokens_pad] (vt_path only)
+  float* mscores = nullptr;  // [B, 16, tokens] F32 (map_fold only)
+  float* zbar = nullptr;     // [B, 16, width] F32 (map_fold only)
 
   // diagnostics
   int capture_layer = -1;
@@ -219,6 +226,50 @@ Gemm make_gemm_block(siglip_model* m, const TensorRef& w, const TensorRef& b, in
   const TensorRef ws = column_block(w, c0, n, wb);
   const TensorRef bs = column_block(b, c0, n, bb);
   return make_gemm(m, ws, bs, staging);
+}
+
+// Constants of the folded MAP head, on the host in float64: q = probe Wq + bq
+// (also kept as F16 for the MAP_Q diagnostic), u_h = W_k,h q_h stored as
+// F16 hi + lo parts in 16 head rows, W_v (transposed per head) and b_v F32.
+void make_map_fold(siglip_model* m, const TensorRef& probe, const TensorRef& qw, const TensorRef& qb,
+                   const TensorRef& kvw, const TensorRef& kvb) {
+  const int W = m->width, H = m->heads, D = m->head_dim;
+  std::vector<double> q(W);
+  for (int n = 0; n < W; ++n) q[n] = qb.host[n];
+  for (int k = 0; k < W; ++k) {
+    const double p = probe.host[k];
+    const float* wr = qw.host + (int64_t)k * W;
+    for (int n = 0; n < W; ++n) q[n] += p * wr[n];
+  }
+  std::vector<f16> qh(W), uh((size_t)16 * W, (f16)0.0f), ul((size_t)16 * W, (f16)0.0f);
+  for (int n = 0; n < W; ++n) qh[n] = (f16)q[n];
+  for (int k = 0; k < W; ++k) {
+    const float* wr = kvw.host + (int64_t)k * 2 * W;  // K block: columns 0 .. W-1
+    for (int h = 0; h < H; ++h) {
+      double u = 0.0;
+      for (int d = 0; d < D; ++d) u += (double)wr[h * D + d] * q[h * D + d];
+      const f16 hi = (f16)u;
+      uh[(size_t)h * W + k] = hi;
+      ul[(size_t)h * W + k] = (f16)(u - (double)hi);
+    }
+  }
+  // W_v transposed per head: wvt[(h*D + d) * W + k] = W_v[k][h*D + d]
+  std::vector<float> wv((size_t)W * W), bv(W);
+  for (int k = 0; k < W; ++k) {
+    const float* vr = kvw.host + (int64_t)k * 2 * W + W;
+    for (int n = 0; n < W; ++n) wv[(size_t)n * W + k] = vr[n];
+  }
+  std::memcpy(bv.data(), kvb.host + W, (size_t)W * 4);
+  m->map_q = static_cast<f16*>(m->dalloc((size_t)W * 2));
+  m->u_hi = static_cast<f16*>(m->dalloc(uh.size() * 2));
+  m->u_lo = static_cast<f16*>(m->dalloc(ul.size() * 2));
+  m->wv = static_cast<float*>(m->dalloc(wv.size() * 4));
+  m->bv = static_cast<float*>(m->dalloc(bv.size() * 4));
+  hip_check(hipMemcpy(m->map_q, qh.data(), qh.size() * 2, hipMemcpyHostToDevice), "hipMemcpy");
+  hip_check(hipMemcpy(m->u_hi, uh.data(), uh.size() * 2, hipMemcpyHostToDevice), "hipMemcpy");
+  hip_check(hipMemcpy(m->u_lo, ul.data(), ul.size() * 2, hipMemcpyHostToDevice), "hipMemcpy");
+  hip_check(hipMemcpy(m->wv, wv.data(), wv.size() * 4, hipMemcpyHostToDevice), "hipMemcpy");
+  hip_check(hipMemcpy(m->bv, bv.data(), bv.size() * 4, hipMemcpyHostToDevice), "hipMemcpy");
 }
 
 void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, void* c, int64_t ldc, int epi,
@@ -326,7 +377,8 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
   int32_t b = 2;
   switch (stage) {
     case SIGLIP_STAGE_EMBED: case SIGLIP_STAGE_H_ATTN: case SIGLIP_STAGE_H_OUT: break;
-    case SIGLIP_STAGE_LN1: case SIGLIP_STAGE_ATTN: case SIGLIP_STAGE_LN2: case SIGLIP_STAGE_FINAL_LN: b = e; break;
+    case SIGLIP_STAGE_LN1: case SIGLIP_STAGE_ATTN: case SIGLIP_STAGE_LN2: b = e; break;
+    case SIGLIP_STAGE_FINAL_LN: b = m->map_fold ? 2 : e; break;
     case SIGLIP_STAGE_QKV: l = 3LL * m->width; c = m->vt_path ? 2LL * m->width : l; break;
     case SIGLIP_STAGE_V_T:
       r = m->vt_path ? (int64_t)batch * m->heads * m->head_dim : 0;
@@ -334,7 +386,7 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
       l = m->tokens_pad;
       break;
     case SIGLIP_STAGE_MLP_HIDDEN: c = m->mlp; l = m->mlp_pad; b = e; break;
-    case SIGLIP_STAGE_MAP_KV: c = l = 2LL * m->width; break;
+    case SIGLIP_STAGE_MAP_KV: c = l = 2LL * m->width; r = m->map_fold ? 0 : M; break;
     case SIGLIP_STAGE_MAP_ATTN: case SIGLIP_STAGE_MAP_LN: r = batch; b = e; break;
     case SIGLIP_STAGE_MAP_Y: r = batch; break;
     case SIGLIP_STAGE_MAP_HIDDEN: r = batch; c = m->mlp; l = m->mlp_pad; b = e; break;
@@ -456,6 +508,27 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     if (ci) capture(m, SIGLIP_STAGE_H_OUT, m->h, cb(SIGLIP_STAGE_H_OUT), s);
   }
 
+  if (m->map_fold) {
+    // Z in F16 (the QKV buffer is free now), then the folded MAP attention
+    f16* z = m->qkv;
+    {
+      LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
+      hip_check(launch_layernorm(m->h, W, z, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, false, 1.0f, s), "final ln");
+    }
+    if (cap) capture(m, SIGLIP_STAGE_FINAL_LN, z, cb(SIGLIP_STAGE_FINAL_LN), s);
+    {
+      LaunchTimer lt(m, SIGLIP_K_MAP_KV, s);
+      hip_check(launch_map_fold(z, W, m->u_hi, m->u_lo, m->wv, m->bv, m->mscores, m->zbar, B, m->tokens, m->heads,
+                                m->head_dim, W, attn_scale, q8, m->op_scale, m->mo, W, s, 0),
+                "map scores");
+    }
+    {
+      LaunchTimer lt(m, SIGLIP_K_MAP_ATTENTION, s);
+      hip_check(launch_map_fold(z, W, m->u_hi, m->u_lo, m->wv, m->bv, m->mscores, m->zbar, B, m->tokens, m->heads,
+                                m->head_dim, W, attn_scale, q8, m->op_scale, m->mo, W, s, 1),
+                "map pool");
+    }
+  } else {
   {
     LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
     hip_check(launch_layernorm(m->h, W, m->a, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, q8, m->op_scale, s), "final ln");
@@ -477,6 +550,7 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     hip_check(launch_map_attention(m->map_q, kv, 2 * W, W, m->mo, W, B, m->heads, m->tokens, m->head_dim, attn_scale,
                                    q8, m->op_scale, s),
               "map attention");
+  }
   }
   if (cap) capture(m, SIGLIP_STAGE_MAP_ATTN, m->mo, cb(SIGLIP_STAGE_MAP_ATTN), s);
   {
@@ -543,6 +617,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_INVALID_ARG, "fp8_scale_exp must be in -8..8");
   if (opt->separate_qkv != 0 && opt->separate_qkv != 1)
     return fail(SIGLIP_E_INVALID_ARG, "separate_qkv must be 0 or 1");
+  if (opt->map_explicit_kv != 0 && opt->map_explicit_kv != 1)
+    return fail(SIGLIP_E_INVALID_ARG, "map_explicit_kv must be 0 or 1");
   if (blob_bytes < sizeof(BlobHeader)) return fail(SIGLIP_E_BAD_BLOB, "blob shorter than its 64-byte header");
   BlobHeader h;
   std::memcpy(&h, blob, sizeof h);
@@ -634,6 +710,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->vt_path = flash_attention_vt_supported(m->head_dim);
     m->tokens_pad = (int)round_up(T, 64);
     m->separate_qkv = opt->separate_qkv == 1;
+    m->map_fold = opt->map_explicit_kv == 0 && map_fold_supported(W, m->heads, m->head_dim, T);
 
     const size_t staging_floats = (size_t)std::max<int64_t>({(int64_t)P * W, 3LL * W * W, (int64_t)W * F, (int64_t)T * W});
     float* staging = static_cast<float*>(m->dalloc(staging_floats * 4));
@@ -661,12 +738,16 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     }
     m->lnf_g = upload_f32(m, lfg);
     m->lnf_b = upload_f32(m, lfb);
-    m->mq = make_gemm(m, qw, qb, staging);
-    if (m->separate_qkv) {
-      m->mk = make_gemm_block(m, kvw, kvb, 0, W, staging);
-      m->mv = make_gemm_block(m, kvw, kvb, W, W, staging);
+    if (m->map_fold) {
+      make_map_fold(m, probe, qw, qb, kvw, kvb);
     } else {
-      m->mkv = make_gemm(m, kvw, kvb, staging);
+      m->mq = make_gemm(m, qw, qb, staging);
+      if (m->separate_qkv) {
+        m->mk = make_gemm_block(m, kvw, kvb, 0, W, staging);
+        m->mv = make_gemm_block(m, kvw, kvb, W, W, staging);
+      } else {
+        m->mkv = make_gemm(m, kvw, kvb, staging);
+      }
     }
     m->mout = make_gemm(m, ow, ob, staging);
     m->mmlp1 = make_gemm(m, m1w, m1b, staging);
@@ -684,6 +765,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
         {(void**)&m->qkv, M * 3 * W * 2}, {&m->o, M * W * es}, {&m->u, M * m->mlp_pad * es},
         {&m->mo, B * W * es}, {(void**)&m->my, B * W * 2}, {&m->ma, B * W * es}, {&m->mu, B * m->mlp_pad * es},
         {(void**)&m->vt, m->vt_path ? B * W * m->tokens_pad * 2 : 0},
+        {(void**)&m->mscores, m->map_fold ? M * 16 * 4 : 0},
+        {(void**)&m->zbar, m->map_fold ? B * 16 * W * 4 : 0},
     };
     size_t total = 0;
     for (auto& p : parts) total += (size_t)round_up(p.bytes, 256);
@@ -695,13 +778,16 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
       off += (size_t)round_up(p.bytes, 256);
     }
 
-    // probe query, once: q = probe Wq + bq (same GEMM as every projection)
+    // probe query, once: q = probe Wq + bq (same GEMM as every projection;
+    // the folded path computed it on the host with the fold constants)
+    if (!m->map_fold) {
     void* probe_op = m->dalloc((size_t)m->mq.k_pad * es);
     hip_check(hipMemcpy(staging, probe.host, (size_t)W * 4, hipMemcpyHostToDevice), "hipMemcpy");
     hip_check(launch_f32_convert(staging, 1, W, probe_op, m->mq.k_pad, m->fp8, m->fp8 ? m->op_scale : 1.0f, nullptr),
               "probe convert");
     m->map_q = static_cast<f16*>(m->dalloc((size_t)m->mq.n_pad * 2));
     gemm(m, m->mq, probe_op, m->mq.k_pad, 1, m->map_q, m->mq.n_pad, EPI_BIAS, false, nullptr, 0, nullptr);
+    }
     hip_check(hipDeviceSynchronize(), "create sync");
   } catch (const HipFail& f) {
     delete m;
