@@ -114,10 +114,12 @@ SIGLIP_API int siglip_create(const void* blob, size_t blob_bytes,
  *
  * pixels_f16: device, [batch, tokens, patch_dim] F16 contiguous, in
  *             [batch, patch_y, patch_x, y, x, channel] order (page
- *             "Single-layer SigLIP vision benchmark", intro). Read only.
+ *             "Single-layer SigLIP vision benchmark", intro). Read only;
+ *             8-byte aligned.
  * batch:      1..max_batch.
  * out_f16:    device, [batch, 1, width] F16 contiguous (page "Single-layer
- *             SigLIP vision benchmark", intro: the probe axis is kept).
+ *             SigLIP vision benchmark", intro: the probe axis is kept);
+ *             16-byte aligned (rows are written in 16-byte chunks).
  * hip_stream: stream to enqueue on.
  * The model's workspace is shared by its calls: calls on one model must be
  * ordered (one stream, or explicit synchronisation). Results are bitwise

@@ -455,6 +455,9 @@ def test_encode_argument_errors(V):
     st = lib.siglip_encode(model.handle, x.data_ptr(), 3, out.data_ptr(), None)
     assert st == V.SIGLIP_E_INVALID_ARG and "max_batch" in V.last_error()
     assert lib.siglip_encode(model.handle, x.data_ptr(), 0, out.data_ptr(), None) == V.SIGLIP_E_INVALID_ARG
+    # the output is written in 16-byte row chunks: an 8-byte aligned view is refused
+    st = lib.siglip_encode(model.handle, x.data_ptr(), 1, out.data_ptr() + 8, None)
+    assert st == V.SIGLIP_E_INVALID_ARG and "aligned" in V.last_error()
     assert lib.siglip_debug_capture(model.handle, 5) == V.SIGLIP_E_INVALID_ARG
 
 

@@ -27,6 +27,8 @@
 // and residual and writes the output 4 columns (8 bytes F16) at a time.
 #include "common.h"
 
+#include <type_traits>
+
 namespace siglip {
 namespace {
 
@@ -53,6 +55,14 @@ struct Tile {
 // & 1) does that (and is also a bijection on any 8 aligned rows).
 __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
+
+// Element type of the output tile staged in LDS: F32 while a residual is
+// still to be added (one rounding), else the output type.
+template <int EPI, bool OUT_FP8>
+struct StageType {
+  typedef typename std::conditional<EPI == EPI_BIAS_RES, float,
+                                    typename std::conditional<OUT_FP8, uint8_t, f16>::type>::type type;
+};
 
 // Linear workgroup id -> output tile. Workgroups are dispatched round-robin
 // over the 8 XCDs (id % 8), each with its own 4 MB L2. The remap gives every
@@ -252,42 +262,83 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
       return;
     }
   }
+  // Output through LDS. The MFMA layout gives each lane 4-column pieces of
+  // 32 different rows, so direct stores write 4 or 8 bytes per row per
+  // instruction. Instead every wave puts its values (bias, positional
+  // embedding and GELU applied; with a residual still to come, kept F32) into
+  // the tile staged in the now idle LDS ring, then the workgroup writes whole
+  // 16-byte chunks of output rows, consecutive threads covering consecutive
+  // chunks, adding the residual there from 16-byte loads. Staged rows are
+  // swizzled in 16-byte chunks by row so the column-wise writes of 16 rows
+  // hit distinct banks.
+  using SType = typename StageType<EPI, OUT_FP8>::type;
+  constexpr int SB = sizeof(SType);
+  constexpr int SROW = BN * SB;  // staged bytes per row
+  constexpr int SCH = SROW / 16;
+  constexpr int SWZ = (SCH < 16 ? SCH : 16) - 1;
+  static_assert(BM * SROW <= STAGES * T::STAGE, "the staged tile fits the LDS ring");
+  auto saddr = [&](int r, int byte) -> uint8_t* {
+    return smem + r * SROW + ((((byte >> 4) ^ (r & SWZ)) << 4) | (byte & 15));
+  };
+  __syncthreads();  // every wave is done with the ring (no transfer is outstanding)
 #pragma unroll
   for (int i = 0; i < T::TM; ++i) {
-    const int m = m0 + wm * WM + i * 32 + fr;
-    if (m >= g.M) continue;
+    const int r = wm * WM + i * 32 + fr;
+    const int m = m0 + r;
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * fg;
+        const int c = wn * WN + j * 32 + 8 * q + 4 * fg;
+        const int n = n0 + c;
         const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + n);
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] * g.acc_scale + b[r];
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * g.acc_scale + b[e];
         if constexpr (EPI == EPI_BIAS_POS) {
           const f32x4 p = *reinterpret_cast<const f32x4*>(g.pos + (int64_t)(m % g.pos_rows) * g.ldpos + n);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] += p[r];
-        }
-        if constexpr (EPI == EPI_BIAS_RES) {
-          const f16x4 rr = *reinterpret_cast<const f16x4*>(g.res + (int64_t)m * g.ldres + n);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] += (float)rr[r];
+          for (int e = 0; e < 4; ++e) v[e] += p[e];
         }
         if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = gelu_tanh(v[r]);
+          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
         }
-        if constexpr (OUT_FP8) {
-          uint32_t w4 = pack4_e4m3(v[0] * g.out_scale, v[1] * g.out_scale,
-                                   v[2] * g.out_scale, v[3] * g.out_scale);
-          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(g.c) + (int64_t)m * g.ldc + n) = w4;
+        if constexpr (SB == 4) {
+          *reinterpret_cast<f32x4*>(saddr(r, 4 * c)) = f32x4{v[0], v[1], v[2], v[3]};
+        } else if constexpr (SB == 2) {
+          *reinterpret_cast<f16x4*>(saddr(r, 2 * c)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
         } else {
-          f16x4 o = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-          *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(g.c) + (int64_t)m * g.ldc + n) = o;
+          *reinterpret_cast<uint32_t*>(saddr(r, c)) =
+              pack4_e4m3(v[0] * g.out_scale, v[1] * g.out_scale, v[2] * g.out_scale, v[3] * g.out_scale);
         }
       }
+    }
+  }
+  __syncthreads();
+  constexpr int OB = OUT_FP8 ? 1 : 2;
+  constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
+  constexpr int VPC = 16 / OB;       // values per output chunk
+#pragma unroll 4
+  for (int u = t; u < BM * OCH; u += T::THREADS) {
+    const int r = u / OCH;
+    const int c = (u - r * OCH) * VPC;
+    const int m = m0 + r;
+    if (m >= g.M) continue;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + ((int64_t)m * g.ldc + n0 + c) * OB;
+    if constexpr (SB == 4) {  // F32 staged, residual added here, F16 out
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(saddr(r, 4 * c));
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(saddr(r, 4 * c + 16));
+      const f16x8 rr = *reinterpret_cast<const f16x8*>(g.res + (int64_t)m * g.ldres + n0 + c);
+      f16x8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] = (f16)(lo[e] + (float)rr[e]);
+        o[e + 4] = (f16)(hi[e] + (float)rr[e + 4]);
+      }
+      *reinterpret_cast<f16x8*>(dst) = o;
+    } else {
+      *reinterpret_cast<i32x4*>(dst) = *reinterpret_cast<const i32x4*>(saddr(r, c * SB));
     }
   }
 }
@@ -310,7 +361,11 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // fill the 256 CUs.
   const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
   if (tiles_128 >= 1024) {
-    if (g.N % 256 == 0) return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(g, s);
+    // 256x256 tiles: not for the residual epilogue (its F32 staged tile
+    // would not fit the LDS ring) nor the V-transposing one (a tile must not
+    // straddle the V column boundary)
+    if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV)
+      if (g.N % 256 == 0) return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(g, s);
     return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8>(g, s);
   }
   if (tiles_128 >= 384) return launch_cfg<128, 128, 64, 64, 2, FP8, EPI, OUT_FP8>(g, s);
@@ -342,6 +397,14 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   if ((int64_t)g.M * g.lda * E >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   if (out_fp8 && epi != EPI_BIAS_GELU) return hipErrorInvalidValue;
+  // 16-byte transfers: operand rows, output rows and residual rows aligned
+  const int OB = out_fp8 ? 1 : 2;
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * E) % 16 || (g.ldw * E) % 16 ||
+      (g.ldc * OB) % 16)
+    return hipErrorInvalidValue;
+  if (epi == EPI_BIAS_RES && (!g.res || misaligned(g.res) || g.ldres % 8 || g.ldres < g.N))
+    return hipErrorInvalidValue;
   if (epi == EPI_QKV && (!g.vt || g.vt_dim < 4 || g.vt_dim % 4 || g.vt_dim > 1024 || g.vt_col0 % 128 ||
                          g.vt_tokens < 1 || g.vt_ld < g.vt_tokens || g.N >= (1 << 20) ||
                          (g.N - g.vt_col0) != g.vt_heads * g.vt_dim))

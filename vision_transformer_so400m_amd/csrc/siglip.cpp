@@ -822,8 +822,8 @@ SIGLIP_API int siglip_encode(siglip_model* m, const void* pixels_f16, int32_t ba
   if (batch < 1 || batch > m->max_batch)
     return fail(SIGLIP_E_INVALID_ARG, "batch " + std::to_string(batch) + " outside 1..max_batch (" +
                                           std::to_string(m->max_batch) + ")");
-  if ((reinterpret_cast<uintptr_t>(pixels_f16) & 7) || (reinterpret_cast<uintptr_t>(out_f16) & 7))
-    return fail(SIGLIP_E_INVALID_ARG, "input and output must be 8-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(pixels_f16) & 7) || (reinterpret_cast<uintptr_t>(out_f16) & 15))
+    return fail(SIGLIP_E_INVALID_ARG, "input must be 8-byte and output 16-byte aligned");
   try {
     encode_impl(m, static_cast<const f16*>(pixels_f16), batch, static_cast<f16*>(out_f16),
                 static_cast<hipStream_t>(hip_stream));
