@@ -361,12 +361,20 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // fill the 256 CUs.
   const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
   if (tiles_128 >= 1024) {
+    // Large grids walk tiles in bands of row blocks (tile_of) unless the
+    // caller chose a band: 4 row blocks of 256, 8 of 128 (measured at
+    // 46,656 rows: 1-3% over row-block-major order).
+    GemmArgs b = g;
     // 256x256 tiles: not for the residual epilogue (its F32 staged tile
     // would not fit the LDS ring) nor the V-transposing one (a tile must not
     // straddle the V column boundary)
     if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV)
-      if (g.N % 256 == 0) return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(g, s);
-    return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8>(g, s);
+      if (g.N % 256 == 0) {
+        if (b.group_m == 0) b.group_m = 4;
+        return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(b, s);
+      }
+    if (b.group_m == 0) b.group_m = 8;
+    return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8>(b, s);
   }
   if (tiles_128 >= 384) return launch_cfg<128, 128, 64, 64, 2, FP8, EPI, OUT_FP8>(g, s);
   return launch_cfg<64, 64, 32, 32, 3, FP8, EPI, OUT_FP8>(g, s);
