@@ -94,62 +94,97 @@ __device__ __forceinline__ float row4_sum(float v) {
 }
 
 // One workgroup of 512 threads (8 waves) per (64-column block, image).
-// First each wave takes two heads: softmax statistics over the tokens (max,
-// then exp2 and sum in F32), probabilities to LDS as [token][16]. Then thread
-// (c, q) = (tid / 16, tid % 16) takes the tokens t = c (mod 32) and
+// Thread (c, q) = (tid / 16, tid % 16) takes the tokens t = c (mod 32) and
 // columns c0 + 4q .. +3 for all 16 head slots (64 accumulators): one 8-byte
-// load of Z per token. The four token slices of a wave are summed by lane
-// exchanges, the 8 waves through LDS.
+// load of Z per token, kRound tokens per round, the next round's loads in
+// flight while the current one is summed. The first round is issued before
+// the softmax: each wave takes two heads, holds a lane's share of the scores
+// in registers (all loads issued together), then max, exp2 and sum in F32;
+// the probabilities go to LDS as rows of kPStride floats per token (16 head
+// slots, padded so that the column writes spread over the banks). The four
+// token slices of a wave are summed by lane exchanges, the 8 waves through
+// LDS.
 constexpr int kPoolThreads = 512;
 constexpr int kPoolWaves = kPoolThreads / 64;
 constexpr int kPoolSlices = kPoolThreads / 16;
+constexpr int kPoolRound = 8;                            // tokens per thread per round
+constexpr int kPoolStep = kPoolRound * kPoolSlices;      // tokens per round per workgroup
+constexpr int kPStride = 20;                             // floats per probability row
+constexpr int kMaxTokens = 1024;
+constexpr int kScorePerLane = kMaxTokens / 64;
 
 __global__ __launch_bounds__(kPoolThreads) void map_pool_kernel(const f16* __restrict__ z, int64_t ldz,
                                                         const float* __restrict__ s, int T, int heads,
                                                         float* __restrict__ zbar, int width) {
-  extern __shared__ float p[];  // [T][kMapHeads]; reused for the wave partials [waves][16][64]
+  extern __shared__ float p[];  // [T][kPStride]; reused for the wave partials [waves][16][64]
+  __shared__ float inv_l[kMapHeads];
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
-  __shared__ float inv_l[kMapHeads];
-  for (int h = tid >> 6; h < kMapHeads; h += kPoolWaves) {
-    const int lane = tid & 63;
-    const float* sh = s + ((int64_t)b * kMapHeads + h) * T;  // this image's scores of head h
-    float m = -__builtin_inff();
-    for (int t = lane; t < T; t += 64) m = fmaxf(m, sh[t]);
-    m = wave_max(m);
-    float l = 0.f;
-    for (int t = lane; t < T; t += 64) {
-      const float e = __builtin_amdgcn_exp2f(sh[t] - m);
-      p[t * kMapHeads + h] = e;
-      l += e;
+  const int c = tid >> 4;
+  const int q = tid & 15;
+  const f16* zc = z + (int64_t)b * T * ldz + blockIdx.x * 64 + 4 * q;
+
+  f16x4 zv[kPoolRound];
+#pragma unroll
+  for (int j = 0; j < kPoolRound; ++j) {
+    const int t = c + kPoolSlices * j;
+    zv[j] = t < T ? *reinterpret_cast<const f16x4*>(zc + (int64_t)t * ldz) : f16x4{0, 0, 0, 0};
+  }
+
+  {
+    const int wave = tid >> 6, lane = tid & 63;
+    const int h0 = 2 * wave;  // heads h0 and h0 + 1
+    const float* s0 = s + ((int64_t)b * kMapHeads + h0) * T;
+    float v0[kScorePerLane], v1[kScorePerLane];
+#pragma unroll
+    for (int i = 0; i < kScorePerLane; ++i) {
+      const int t = lane + 64 * i;
+      v0[i] = t < T ? s0[t] : -__builtin_inff();
+      v1[i] = t < T ? s0[T + t] : -__builtin_inff();
     }
-    l = wave_sum(l);
-    if (lane == 0) inv_l[h] = 1.0f / l;
+    float m0 = v0[0], m1 = v1[0];
+#pragma unroll
+    for (int i = 1; i < kScorePerLane; ++i) {
+      m0 = fmaxf(m0, v0[i]);
+      m1 = fmaxf(m1, v1[i]);
+    }
+    m0 = wave_max(m0);
+    m1 = wave_max(m1);
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kScorePerLane; ++i) {
+      const int t = lane + 64 * i;
+      const float e0 = __builtin_amdgcn_exp2f(v0[i] - m0);  // exactly 0 past the end
+      const float e1 = __builtin_amdgcn_exp2f(v1[i] - m1);
+      if (t < T) *reinterpret_cast<float2*>(p + t * kPStride + h0) = float2{e0, e1};
+      l0 += e0;
+      l1 += e1;
+    }
+    l0 = wave_sum(l0);
+    l1 = wave_sum(l1);
+    if (lane == 0) {
+      inv_l[h0] = 1.0f / l0;
+      inv_l[h0 + 1] = 1.0f / l1;
+    }
   }
   __syncthreads();
 
-  const int c = tid >> 4;
-  const int q = tid & 15;
-  const int col = blockIdx.x * 64 + 4 * q;
-  const f16* zc = z + (int64_t)b * T * ldz + col;
   float acc[kMapHeads][4];
 #pragma unroll
   for (int h = 0; h < kMapHeads; ++h)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
-  constexpr int kRound = 8;  // tokens whose loads are in flight together
-  for (int t0 = c; t0 < T; t0 += kRound * kPoolSlices) {
-    f16x4 zv[kRound];
+  for (int t0 = c; t0 < T; t0 += kPoolStep) {
+    f16x4 zn[kPoolRound];
 #pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int t = t0 + kPoolSlices * j;
-      zv[j] = t < T ? *reinterpret_cast<const f16x4*>(zc + (int64_t)t * ldz) : f16x4{0, 0, 0, 0};
+    for (int j = 0; j < kPoolRound; ++j) {
+      const int t = t0 + kPoolStep + kPoolSlices * j;
+      zn[j] = t < T ? *reinterpret_cast<const f16x4*>(zc + (int64_t)t * ldz) : f16x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int t = t0 + kPoolSlices * j;
-      if (t >= T) break;
-      const f32x4* pt = reinterpret_cast<const f32x4*>(p + t * kMapHeads);
+    for (int j = 0; j < kPoolRound; ++j) {
+      const int t = min(t0 + kPoolSlices * j, T - 1);  // tokens past the end carry Z = 0
+      const f32x4* pt = reinterpret_cast<const f32x4*>(p + t * kPStride);
       float zf[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) zf[e] = (float)zv[j][e];
@@ -162,6 +197,8 @@ __global__ __launch_bounds__(kPoolThreads) void map_pool_kernel(const f16* __res
           for (int e = 0; e < 4; ++e) acc[4 * h4 + hh][e] = fmaf(pv[hh], zf[e], acc[4 * h4 + hh][e]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < kPoolRound; ++j) zv[j] = zn[j];
   }
   // lanes q, q+16, q+32, q+48 of a wave hold the four token slices of column quad q
 #pragma unroll
@@ -251,7 +288,7 @@ __global__ __launch_bounds__(1024) void map_vproj_kernel(const float* __restrict
 
 bool map_fold_supported(int width, int heads, int head_dim, int tokens) {
   return heads >= 1 && heads <= kMapHeads && width % 128 == 0 && width <= 4096 && tokens >= 1 &&
-         tokens <= 1024 && head_dim >= 4 && head_dim % 4 == 0 && head_dim * kVprojChunks <= 1024 &&
+         tokens <= kMaxTokens && head_dim >= 4 && head_dim % 4 == 0 && head_dim * kVprojChunks <= 1024 &&
          heads * head_dim == width;
 }
 
@@ -269,8 +306,8 @@ hipError_t launch_map_fold(const f16* z, int64_t ldz, const f16* u_hi, const f16
                        width, scores, rows, tokens, sl2);
     return hipGetLastError();
   }
-  // probabilities [tokens][16] F32, reused for waves x 16 x 16 partial sums of 16 bytes
-  const size_t pool_lds = std::max<size_t>((size_t)kMapHeads * tokens * sizeof(float), kPoolWaves * kMapHeads * 16 * 16);
+  // probabilities [tokens][kPStride] F32, reused for waves x 16 x 16 partial sums of 16 bytes
+  const size_t pool_lds = std::max<size_t>((size_t)kPStride * tokens * sizeof(float), kPoolWaves * kMapHeads * 16 * 16);
   hipLaunchKernelGGL(map_pool_kernel, dim3((unsigned)(width / 64), (unsigned)batch), dim3(kPoolThreads), pool_lds, s, z, ldz,
                      scores, tokens, heads, zbar, width);
   hipError_t e = hipGetLastError();
