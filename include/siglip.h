@@ -121,6 +121,14 @@ SIGLIP_API int siglip_create(const void* blob, size_t blob_bytes,
  *             SigLIP vision benchmark", intro: the probe axis is kept);
  *             16-byte aligned (rows are written in 16-byte chunks).
  * hip_stream: stream to enqueue on.
+ * A batch of two or more images runs as two half-batches: the first half on
+ * hip_stream, the second on a stream the model owns (default priority),
+ * which waits for hip_stream's earlier work and which hip_stream waits for
+ * before its later work, so the call behaves as one ordered unit of
+ * hip_stream. Images are independent, each output row is computed by the
+ * same kernels in the same order either way, and the results are bitwise
+ * identical. Stage capture and launch timing (siglip_debug_*) run the batch
+ * on hip_stream alone.
  * The model's workspace is shared by its calls: calls on one model must be
  * ordered (one stream, or explicit synchronisation). Results are bitwise
  * deterministic run to run. Errors: INVALID_ARG, HIP.
@@ -248,6 +256,8 @@ typedef enum {
  * launches of class k; 0 turns timing off. Each selected launch is bracketed
  * by two HIP events recorded on the call's stream, so its duration is the
  * time between them on the GPU; unselected launches are not perturbed.
+ * While timing is on, siglip_encode runs the whole batch on the call's
+ * stream (no half-batch split), so a launch's duration is its own.
  * Errors: INVALID_ARG. */
 SIGLIP_API int siglip_debug_timing(siglip_model* m, uint32_t class_mask);
 

@@ -407,6 +407,33 @@ def test_determinism_and_nan_poisoned_workspace(V):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
+def test_half_batch_streams_match_one_stream_bitwise(V, fp8):
+    """A call with two or more images runs its halves on two streams; with
+    launch timing on it runs on the caller's stream alone. Both must give
+    the same bits, on the default stream and on a side stream whose later
+    work reads the result (the join must order it after both halves)."""
+    dims = S.SO400M.with_depth(2)
+    _flush(f"half-batch streams fp8={fp8}")
+    model, _ = make_model(V, dims, 5, max_batch=9, fp8=fp8)
+    x = torch.from_numpy(S.make_pixels(dims, 9, 6)).cuda()
+    for b in (2, 3, 9):
+        xb = x[:b].contiguous()
+        split = model.encode(xb).clone()
+        model.debug_timing(["MAP_TAIL"])
+        one = model.encode(xb).clone()
+        model.debug_timing(False)
+        torch.cuda.synchronize()
+        assert torch.equal(split.view(torch.int16), one.view(torch.int16)), b
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            y = model.encode(xb)
+            bits = y.view(torch.int16).clone()  # runs on st after the call's join
+        torch.cuda.synchronize()
+        assert torch.equal(bits, one.view(torch.int16)), b
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
 def test_separate_qkv_matches_fused_bitwise(V, fp8):
     """Separate Q/K/V (and MAP K/V) projections against the fused ones: every
     output element has the same operands and summation order, so results are

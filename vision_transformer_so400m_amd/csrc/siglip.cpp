@@ -159,6 +159,12 @@ struct siglip_model {
   void* cap[SIGLIP_STAGE_COUNT] = {};
   size_t cap_bytes[SIGLIP_STAGE_COUNT] = {};
 
+  // two half-batches on two streams (images are independent): a second
+  // stream of default priority and the events that fork it from the
+  // caller's stream and join it back
+  hipStream_t side = nullptr;
+  hipEvent_t fork_ev = nullptr, join_ev = nullptr;
+
   // per-launch timing: event pairs recorded around launches, resolved on read
   uint32_t timing_mask = 0;               // classes whose launches are timed
   std::vector<hipEvent_t> ev_pool;        // 2 events per pending launch
@@ -170,6 +176,9 @@ struct siglip_model {
 
   ~siglip_model() {
     for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    if (fork_ev) (void)hipEventDestroy(fork_ev);
+    if (join_ev) (void)hipEventDestroy(join_ev);
+    if (side) (void)hipStreamDestroy(side);
     for (void* p : allocs) (void)hipFree(p);
   }
 
@@ -272,6 +281,46 @@ void make_map_fold(siglip_model* m, const TensorRef& probe, const TensorRef& qw,
   hip_check(hipMemcpy(m->bv, bv.data(), bv.size() * 4, hipMemcpyHostToDevice), "hipMemcpy");
 }
 
+// The activation buffers of the images [b0, ...) of a call: every buffer is
+// image-major, so a half-batch works on row (or image) ranges of the same
+// workspace.
+struct Acts {
+  void* xp;
+  f16* h;
+  void* a;
+  f16* qkv;
+  void* o;
+  void* u;
+  void* mo;
+  f16* my;
+  void* ma;
+  void* mu;
+  f16* vt;
+  float* mscores;
+  float* zbar;
+};
+
+Acts acts_at(const siglip_model* m, int b0) {
+  const int64_t r0 = (int64_t)b0 * m->tokens;  // first token row
+  const int64_t W = m->width, es = m->esz();
+  auto at = [](void* p, int64_t bytes) -> void* { return p ? static_cast<uint8_t*>(p) + bytes : nullptr; };
+  Acts A;
+  A.xp = at(m->xp, r0 * m->patch_pad * es);
+  A.h = m->h + r0 * W;
+  A.a = at(m->a, r0 * W * es);
+  A.qkv = m->qkv + r0 * 3 * W;
+  A.o = at(m->o, r0 * W * es);
+  A.u = at(m->u, r0 * m->mlp_pad * es);
+  A.mo = at(m->mo, b0 * W * es);
+  A.my = m->my + b0 * W;
+  A.ma = at(m->ma, b0 * W * es);
+  A.mu = at(m->mu, b0 * m->mlp_pad * es);
+  A.vt = m->vt ? m->vt + (int64_t)b0 * W * m->tokens_pad : nullptr;
+  A.mscores = m->mscores ? m->mscores + r0 * 16 : nullptr;
+  A.zbar = m->zbar ? m->zbar + (int64_t)b0 * 16 * W : nullptr;
+  return A;
+}
+
 void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, void* c, int64_t ldc, int epi,
           bool out_fp8, const f16* res, int64_t ldres, hipStream_t s) {
   GemmArgs args{};
@@ -297,16 +346,16 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
 
 // The fused QKV projection: Q and K row-major into qkv, V transposed per
 // head into vt when the streaming attention is used.
-void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hipStream_t s) {
+void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, f16* vt, int M, hipStream_t s) {
   const Gemm& g = Ly.qkv;
   if (m->separate_qkv) {
     // Q and K into their columns of the fused row; V as its own projection,
     // transposed per head (all its columns are V: vt_col0 = 0)
     const int W = m->width;
-    gemm(m, Ly.q, a, W, M, m->qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
-    gemm(m, Ly.k, a, W, M, m->qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    gemm(m, Ly.q, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    gemm(m, Ly.k, a, W, M, qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
     if (!m->vt_path) {
-      gemm(m, Ly.v, a, W, M, m->qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, Ly.v, a, W, M, qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
       return;
     }
     GemmArgs args{};
@@ -314,7 +363,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hip
     args.lda = W;
     args.w = Ly.v.w;
     args.ldw = Ly.v.k_pad;
-    args.c = m->qkv + 2 * W;  // not written: every column goes to vt
+    args.c = qkv + 2 * W;  // not written: every column goes to vt
     args.ldc = 3 * W;
     args.bias = Ly.v.bias;
     args.M = M;
@@ -322,7 +371,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hip
     args.K = Ly.v.k_pad;
     args.acc_scale = m->acc_scale;
     args.out_scale = m->op_scale;
-    args.vt = m->vt;
+    args.vt = vt;
     args.vt_col0 = 0;
     args.vt_tokens = m->tokens;
     args.vt_heads = m->heads;
@@ -333,7 +382,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hip
     return;
   }
   if (!m->vt_path) {
-    gemm(m, g, a, m->width, M, m->qkv, 3 * m->width, EPI_BIAS, false, nullptr, 0, s);
+    gemm(m, g, a, m->width, M, qkv, 3 * m->width, EPI_BIAS, false, nullptr, 0, s);
     return;
   }
   GemmArgs args{};
@@ -341,7 +390,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hip
   args.lda = m->width;
   args.w = g.w;
   args.ldw = g.k_pad;
-  args.c = m->qkv;
+  args.c = qkv;
   args.ldc = 3 * m->width;
   args.bias = g.bias;
   args.M = M;
@@ -349,7 +398,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hip
   args.K = g.k_pad;
   args.acc_scale = m->acc_scale;
   args.out_scale = m->op_scale;
-  args.vt = m->vt;
+  args.vt = vt;
   args.vt_col0 = 2 * m->width;
   args.vt_tokens = m->tokens;
   args.vt_heads = m->heads;
@@ -360,7 +409,6 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, int M, int B, hip
   // activations: walk tiles in bands of 8 row blocks (measured ~12% faster
   // at 46,656 rows than row-block-major order)
   args.group_m = 8;
-  (void)B;
   hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "qkv gemm launch");
 }
 
@@ -429,7 +477,7 @@ class LaunchTimer {
   size_t pair_ = 0;
 };
 
-void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) {
+void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, hipStream_t s) {
   const int M = B * m->tokens;
   const int W = m->width;
   const int e = m->esz();
@@ -444,20 +492,20 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
 
   {
     LaunchTimer lt(m, SIGLIP_K_INPUT, s);
-    hip_check(launch_pad_convert(x, m->patch_dim, m->xp, M, m->patch_dim, m->patch_pad, q8, q8 ? m->op_scale : 1.0f, s),
+    hip_check(launch_pad_convert(x, m->patch_dim, A.xp, M, m->patch_dim, m->patch_pad, q8, q8 ? m->op_scale : 1.0f, s),
               "pad_convert");
   }
   {
     LaunchTimer lt(m, SIGLIP_K_EMBED, s);
-    gemm(m, m->embed, m->xp, m->patch_pad, M, m->h, W, EPI_BIAS_POS, false, nullptr, 0, s);
+    gemm(m, m->embed, A.xp, m->patch_pad, M, A.h, W, EPI_BIAS_POS, false, nullptr, 0, s);
   }
   if (m->vt_path && m->tokens_pad > m->tokens) {
     // V^T columns past the last token are read by the last key block: zeros
     LaunchTimer lt(m, SIGLIP_K_INPUT, s);
-    hip_check(launch_zero_cols(m->vt, (int64_t)B * m->heads * m->head_dim, m->tokens_pad, m->tokens, m->tokens_pad, s),
+    hip_check(launch_zero_cols(A.vt, (int64_t)B * m->heads * m->head_dim, m->tokens_pad, m->tokens, m->tokens_pad, s),
               "zero V^T tail");
   }
-  if (cap) capture(m, SIGLIP_STAGE_EMBED, m->h, cb(SIGLIP_STAGE_EMBED), s);
+  if (cap) capture(m, SIGLIP_STAGE_EMBED, A.h, cb(SIGLIP_STAGE_EMBED), s);
 
   const float attn_scale = 1.0f / std::sqrt((float)m->head_dim);
   for (int i = 0; i < m->layers; ++i) {
@@ -465,117 +513,139 @@ void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) 
     const bool ci = cap && i == m->capture_layer;
     {
       LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-      hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
+      hip_check(launch_layernorm(A.h, W, A.a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
     }
-    if (ci) capture(m, SIGLIP_STAGE_LN1, m->a, cb(SIGLIP_STAGE_LN1), s);
+    if (ci) capture(m, SIGLIP_STAGE_LN1, A.a, cb(SIGLIP_STAGE_LN1), s);
     {
       LaunchTimer lt(m, SIGLIP_K_QKV, s);
-      gemm_qkv(m, Ly, m->a, M, B, s);
+      gemm_qkv(m, Ly, A.a, A.qkv, A.vt, M, s);
     }
-    if (ci) capture(m, SIGLIP_STAGE_QKV, m->qkv, cb(SIGLIP_STAGE_QKV), s);
-    if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, m->vt, cb(SIGLIP_STAGE_V_T), s);
+    if (ci) capture(m, SIGLIP_STAGE_QKV, A.qkv, cb(SIGLIP_STAGE_QKV), s);
+    if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, A.vt, cb(SIGLIP_STAGE_V_T), s);
     {
       LaunchTimer lt(m, SIGLIP_K_ATTENTION, s);
       if (m->vt_path)
-        hip_check(launch_flash_attention_vt(m->qkv, m->qkv + W, 3 * W, m->vt, m->tokens_pad, m->o, W, B, m->heads,
+        hip_check(launch_flash_attention_vt(A.qkv, A.qkv + W, 3 * W, A.vt, m->tokens_pad, A.o, W, B, m->heads,
                                             m->tokens, m->head_dim, attn_scale, q8, m->op_scale, s),
                   "attention");
       else
-        hip_check(launch_flash_attention(m->qkv, m->qkv + W, m->qkv + 2 * W, 3 * W, m->o, W, B, m->heads, m->tokens,
+        hip_check(launch_flash_attention(A.qkv, A.qkv + W, A.qkv + 2 * W, 3 * W, A.o, W, B, m->heads, m->tokens,
                                          m->head_dim, attn_scale, q8, m->op_scale, s),
                   "attention");
     }
-    if (ci) capture(m, SIGLIP_STAGE_ATTN, m->o, cb(SIGLIP_STAGE_ATTN), s);
+    if (ci) capture(m, SIGLIP_STAGE_ATTN, A.o, cb(SIGLIP_STAGE_ATTN), s);
     {
       LaunchTimer lt(m, SIGLIP_K_OUT_PROJ, s);
-      gemm(m, Ly.out, m->o, W, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+      gemm(m, Ly.out, A.o, W, M, A.h, W, EPI_BIAS_RES, false, A.h, W, s);
     }
-    if (ci) capture(m, SIGLIP_STAGE_H_ATTN, m->h, cb(SIGLIP_STAGE_H_ATTN), s);
+    if (ci) capture(m, SIGLIP_STAGE_H_ATTN, A.h, cb(SIGLIP_STAGE_H_ATTN), s);
     {
       LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-      hip_check(launch_layernorm(m->h, W, m->a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
+      hip_check(launch_layernorm(A.h, W, A.a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
     }
-    if (ci) capture(m, SIGLIP_STAGE_LN2, m->a, cb(SIGLIP_STAGE_LN2), s);
+    if (ci) capture(m, SIGLIP_STAGE_LN2, A.a, cb(SIGLIP_STAGE_LN2), s);
     {
       LaunchTimer lt(m, SIGLIP_K_MLP_UP, s);
-      gemm(m, Ly.mlp1, m->a, W, M, m->u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+      gemm(m, Ly.mlp1, A.a, W, M, A.u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
     }
-    if (ci) capture(m, SIGLIP_STAGE_MLP_HIDDEN, m->u, cb(SIGLIP_STAGE_MLP_HIDDEN), s);
+    if (ci) capture(m, SIGLIP_STAGE_MLP_HIDDEN, A.u, cb(SIGLIP_STAGE_MLP_HIDDEN), s);
     {
       LaunchTimer lt(m, SIGLIP_K_MLP_DOWN, s);
-      gemm(m, Ly.mlp2, m->u, m->mlp_pad, M, m->h, W, EPI_BIAS_RES, false, m->h, W, s);
+      gemm(m, Ly.mlp2, A.u, m->mlp_pad, M, A.h, W, EPI_BIAS_RES, false, A.h, W, s);
     }
-    if (ci) capture(m, SIGLIP_STAGE_H_OUT, m->h, cb(SIGLIP_STAGE_H_OUT), s);
+    if (ci) capture(m, SIGLIP_STAGE_H_OUT, A.h, cb(SIGLIP_STAGE_H_OUT), s);
   }
 
   if (m->map_fold) {
     // Z in F16 (the QKV buffer is free now), then the folded MAP attention
-    f16* z = m->qkv;
+    f16* z = A.qkv;
     {
       LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-      hip_check(launch_layernorm(m->h, W, z, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, false, 1.0f, s), "final ln");
+      hip_check(launch_layernorm(A.h, W, z, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, false, 1.0f, s), "final ln");
     }
     if (cap) capture(m, SIGLIP_STAGE_FINAL_LN, z, cb(SIGLIP_STAGE_FINAL_LN), s);
     {
       LaunchTimer lt(m, SIGLIP_K_MAP_KV, s);
-      hip_check(launch_map_fold(z, W, m->u_hi, m->u_lo, m->wv, m->bv, m->mscores, m->zbar, B, m->tokens, m->heads,
-                                m->head_dim, W, attn_scale, q8, m->op_scale, m->mo, W, s, 0),
+      hip_check(launch_map_fold(z, W, m->u_hi, m->u_lo, m->wv, m->bv, A.mscores, A.zbar, B, m->tokens, m->heads,
+                                m->head_dim, W, attn_scale, q8, m->op_scale, A.mo, W, s, 0),
                 "map scores");
     }
     {
       LaunchTimer lt(m, SIGLIP_K_MAP_ATTENTION, s);
-      hip_check(launch_map_fold(z, W, m->u_hi, m->u_lo, m->wv, m->bv, m->mscores, m->zbar, B, m->tokens, m->heads,
-                                m->head_dim, W, attn_scale, q8, m->op_scale, m->mo, W, s, 1),
+      hip_check(launch_map_fold(z, W, m->u_hi, m->u_lo, m->wv, m->bv, A.mscores, A.zbar, B, m->tokens, m->heads,
+                                m->head_dim, W, attn_scale, q8, m->op_scale, A.mo, W, s, 1),
                 "map pool");
     }
   } else {
   {
     LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-    hip_check(launch_layernorm(m->h, W, m->a, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, q8, m->op_scale, s), "final ln");
+    hip_check(launch_layernorm(A.h, W, A.a, W, m->lnf_g, m->lnf_b, M, W, 1e-6f, q8, m->op_scale, s), "final ln");
   }
-  if (cap) capture(m, SIGLIP_STAGE_FINAL_LN, m->a, cb(SIGLIP_STAGE_FINAL_LN), s);
-  f16* kv = m->qkv;  // [M, 2W]
+  if (cap) capture(m, SIGLIP_STAGE_FINAL_LN, A.a, cb(SIGLIP_STAGE_FINAL_LN), s);
+  f16* kv = A.qkv;  // [M, 2W]
   {
     LaunchTimer lt(m, SIGLIP_K_MAP_KV, s);
     if (m->separate_qkv) {
-      gemm(m, m->mk, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
-      gemm(m, m->mv, m->a, W, M, kv + W, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, m->mk, A.a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, m->mv, A.a, W, M, kv + W, 2 * W, EPI_BIAS, false, nullptr, 0, s);
     } else {
-      gemm(m, m->mkv, m->a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, m->mkv, A.a, W, M, kv, 2 * W, EPI_BIAS, false, nullptr, 0, s);
     }
   }
   if (cap) capture(m, SIGLIP_STAGE_MAP_KV, kv, cb(SIGLIP_STAGE_MAP_KV), s);
   {
     LaunchTimer lt(m, SIGLIP_K_MAP_ATTENTION, s);
-    hip_check(launch_map_attention(m->map_q, kv, 2 * W, W, m->mo, W, B, m->heads, m->tokens, m->head_dim, attn_scale,
+    hip_check(launch_map_attention(m->map_q, kv, 2 * W, W, A.mo, W, B, m->heads, m->tokens, m->head_dim, attn_scale,
                                    q8, m->op_scale, s),
               "map attention");
   }
   }
-  if (cap) capture(m, SIGLIP_STAGE_MAP_ATTN, m->mo, cb(SIGLIP_STAGE_MAP_ATTN), s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_ATTN, A.mo, cb(SIGLIP_STAGE_MAP_ATTN), s);
   {
     LaunchTimer lt(m, SIGLIP_K_MAP_TAIL, s);
-    gemm(m, m->mout, m->mo, W, B, m->my, W, EPI_BIAS, false, nullptr, 0, s);
+    gemm(m, m->mout, A.mo, W, B, A.my, W, EPI_BIAS, false, nullptr, 0, s);
   }
-  if (cap) capture(m, SIGLIP_STAGE_MAP_Y, m->my, cb(SIGLIP_STAGE_MAP_Y), s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_Y, A.my, cb(SIGLIP_STAGE_MAP_Y), s);
   {
     LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-    hip_check(launch_layernorm(m->my, W, m->ma, W, m->mln_g, m->mln_b, B, W, 1e-6f, q8, m->op_scale, s), "map ln");
+    hip_check(launch_layernorm(A.my, W, A.ma, W, m->mln_g, m->mln_b, B, W, 1e-6f, q8, m->op_scale, s), "map ln");
   }
-  if (cap) capture(m, SIGLIP_STAGE_MAP_LN, m->ma, cb(SIGLIP_STAGE_MAP_LN), s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_LN, A.ma, cb(SIGLIP_STAGE_MAP_LN), s);
   {
     LaunchTimer lt(m, SIGLIP_K_MAP_TAIL, s);
-    gemm(m, m->mmlp1, m->ma, W, B, m->mu, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+    gemm(m, m->mmlp1, A.ma, W, B, A.mu, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
   }
-  if (cap) capture(m, SIGLIP_STAGE_MAP_HIDDEN, m->mu, cb(SIGLIP_STAGE_MAP_HIDDEN), s);
+  if (cap) capture(m, SIGLIP_STAGE_MAP_HIDDEN, A.mu, cb(SIGLIP_STAGE_MAP_HIDDEN), s);
   {
     LaunchTimer lt(m, SIGLIP_K_MAP_TAIL, s);
-    gemm(m, m->mmlp2, m->mu, m->mlp_pad, B, out, W, EPI_BIAS_RES, false, m->my, W, s);
+    gemm(m, m->mmlp2, A.mu, m->mlp_pad, B, out, W, EPI_BIAS_RES, false, A.my, W, s);
   }
   if (cap) {
     m->captured = true;
     m->captured_batch = B;
   }
+}
+
+// One call: the whole batch on the caller's stream, or (batches of two or
+// more, no stage capture or launch timing) the first half there and the
+// second half on the side stream, forked from and joined back into the
+// caller's stream. The halves share no buffer rows, and the kernels of one
+// can fill the CUs the other leaves idle (the last partial wave of a GEMM's
+// tiles, an attention or LayerNorm phase next to a GEMM).
+void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) {
+  const bool split = B >= 2 && m->side && m->capture_layer < 0 && m->timing_mask == 0;
+  if (!split) {
+    encode_part(m, acts_at(m, 0), x, B, out, s);
+    return;
+  }
+  const int B0 = (B + 1) / 2;
+  hip_check(hipEventRecord(m->fork_ev, s), "fork record");
+  hip_check(hipStreamWaitEvent(m->side, m->fork_ev, 0), "fork wait");
+  encode_part(m, acts_at(m, 0), x, B0, out, s);
+  encode_part(m, acts_at(m, B0), x + (int64_t)B0 * m->tokens * m->patch_dim, B - B0, out + (int64_t)B0 * m->width,
+              m->side);
+  hip_check(hipEventRecord(m->join_ev, m->side), "join record");
+  hip_check(hipStreamWaitEvent(s, m->join_ev, 0), "join wait");
 }
 
 int validate_header(const BlobHeader& h, size_t blob_bytes, std::string* why) {
@@ -777,6 +847,10 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
       *p.dst = static_cast<uint8_t*>(m->ws) + off;
       off += (size_t)round_up(p.bytes, 256);
     }
+
+    hip_check(hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking), "hipStreamCreate");
+    hip_check(hipEventCreateWithFlags(&m->fork_ev, hipEventDisableTiming), "hipEventCreate");
+    hip_check(hipEventCreateWithFlags(&m->join_ev, hipEventDisableTiming), "hipEventCreate");
 
     // probe query, once: q = probe Wq + bq (same GEMM as every projection;
     // the folded path computed it on the host with the fold constants)
