@@ -131,7 +131,8 @@ def sweep(args):
     images/s at B = 1..64 for e4m3 and F16 GEMM operands; the projected-
     attention block (LN + QKV + attention + out-proj) and the MLP block
     (LN + up + down) from per-launch HIP events at B = 1 and B = 64; fused
-    against separate Q/K/V projections."""
+    against separate Q/K/V projections; F16 against e4m3 PV attention
+    products."""
     import torch
 
     import synthetic as S
@@ -143,7 +144,7 @@ def sweep(args):
     del wt
     xall = torch.from_numpy(S.make_pixels(d, 64, 2)).cuda()
     res = {"workload": "SigLIP So400m/14 27 layers + MAP, synthetic seed-2 input and weights", "batches": {}, "blocks": {},
-           "qkv_projections": {}}
+           "qkv_projections": {}, "attention_products": {}}
     batches = [1, 2, 4, 8, 16, 32, 64]
     for fp8 in (True, False):
         tag = "e4m3" if fp8 else "f16"
@@ -176,6 +177,19 @@ def sweep(args):
             qkv_us = ct["QKV"][0] * ct["QKV"][1] / d.depth  # all launches of the class, per layer
             res["qkv_projections"][tag][f"b{b}"] = {"ms": round(ms, 4), "qkv_us_per_layer": round(qkv_us, 2),
                                                     "map_kv_us": round(ct["MAP_KV"][0] * ct["MAP_KV"][1], 2)}
+        model.close()
+    for afp8 in (False, True):
+        model = V.Model(blob, max_batch=64, fp8=True, attention_fp8=afp8)
+        tag = "e4m3_pv" if afp8 else "f16"
+        res["attention_products"][tag] = {}
+        for b in (1, 64):
+            x = xall[:b].contiguous()
+            out = torch.empty((b, 1, d.width), dtype=torch.float16, device="cuda")
+            ms = time_calls(model, x, out, args.sweep_steps if b > 1 else 4 * args.sweep_steps)
+            ct = class_times(model, x, out)
+            res["attention_products"][tag][f"b{b}"] = {"ms": round(ms, 4), "images_per_s": round(b / ms * 1e3, 2),
+                                                       "attention_us": round(ct["ATTENTION"][0], 2),
+                                                       "qkv_us": round(ct["QKV"][0], 2)}
         model.close()
     print(json.dumps(res), flush=True)
 

@@ -134,6 +134,20 @@ def test_bad_map_explicit_kv_value(blob1):
     assert b"map_explicit_kv" in lib.siglip_last_error()
 
 
+def test_bad_attention_fp8_value(blob1):
+    lib = V.load_library()
+    out = ctypes.c_void_p()
+    opt = V.siglip_options(0, 1, 0, -4, 0, 0, 2)
+    st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
+    assert st == V.SIGLIP_E_INVALID_ARG and not out.value
+    assert b"attention_fp8" in lib.siglip_last_error()
+    # its scale exponent is checked even with F16 GEMM operands
+    opt = V.siglip_options(0, 1, 0, 9, 0, 0, 1)
+    st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
+    assert st == V.SIGLIP_E_INVALID_ARG and not out.value
+    assert b"fp8_scale_exp" in lib.siglip_last_error()
+
+
 def test_unsupported_width_is_reported_before_the_device():
     d = S.small_dims(1)   # width 144: not a multiple of 128
     e = _create(bytes(S.pack_blob(d, S.make_weights(d, 0))))

@@ -46,7 +46,8 @@ class SiglipError(RuntimeError):
 class siglip_options(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("gemm_precision", ctypes.c_int32), ("fp8_scale_exp", ctypes.c_int32),
-                ("separate_qkv", ctypes.c_int32), ("map_explicit_kv", ctypes.c_int32)]
+                ("separate_qkv", ctypes.c_int32), ("map_explicit_kv", ctypes.c_int32),
+                ("attention_fp8", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -113,11 +114,12 @@ class Model:
     """A resident encoder: weights uploaded once by siglip_create."""
 
     def __init__(self, blob, layers: int = 0, max_batch: int = 1, fp8: bool = False,
-                 fp8_scale_exp: int = -4, separate_qkv: bool = False, map_explicit_kv: bool = False):
+                 fp8_scale_exp: int = -4, separate_qkv: bool = False, map_explicit_kv: bool = False,
+                 attention_fp8: bool = False):
         lib = load_library()
         keep, ptr, n = _host_ptr(blob)
         opt = siglip_options(layers, max_batch, 1 if fp8 else 0, fp8_scale_exp, 1 if separate_qkv else 0,
-                             1 if map_explicit_kv else 0)
+                             1 if map_explicit_kv else 0, 1 if attention_fp8 else 0)
         h = ctypes.c_void_p()
         _check(lib.siglip_create(ptr, n, ctypes.byref(opt), ctypes.byref(h)))
         self._h = h

@@ -520,6 +520,249 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// e4m3 PV product (page "FP8 attention and resident image/embedding
+// transfers": F143 operands at scale -4 for the PV product, with the softmax,
+// its F32 state and the output precision unchanged; "Full 27-layer ViT": a
+// profitable form has the producers write the quantized operands). Here the
+// QKV GEMM epilogue writes V^T as e4m3 codes of v * 2^-exp and the
+// probabilities are quantized in registers as e4m3 codes of p * 2^4, so no
+// cast pass exists; one v_mfma_scale_f32_32x32x64_f8f6f4 per 32 head dims
+// covers a whole 64-key block (four F16 MFMAs otherwise). QK stays F16.
+//
+// Same work split and K streaming as flash_attn_vt_kernel, with another K row
+// order: tile kt row i holds key 32 ((i >> 2) & 1) + 16 kt + 4 (i >> 3) + (i & 3),
+// so lane group g of a score tile holds the keys 32 g + 16 kt + r (r = 0..15)
+// and its 32 probabilities of the block are keys 32 g .. 32 g + 31 in order:
+// the P^T fragment of the MFMA, and the matching V^T fragment is bytes
+// 32 g .. 32 g + 31 of a V^T row (two 16-byte LDS reads).
+//
+// V^T stage: 80 rows of 64 key bytes, 16-byte chunks swizzled by
+// (row >> 2) & 3 (16 consecutive rows read one chunk without bank conflicts).
+// Rows D..79 are read from the rows that follow the head's D rows in memory
+// (the next head's, or the buffer's slack after the last); they reach only
+// rows D..79 of O^T, which are never read. Row 80 holds e4m3(2^-exp), so the
+// same MFMA yields each query's sum of its quantized probabilities (the scales
+// 2^4 and 2^-exp cancel in the division); rows 81..95 are zero.
+//
+// The probabilities stay <= 2^4: the running reference moves when a block's
+// maximum exceeds it by more than 4 in exp2 units, so 2^4 p <= 256 < 448 and
+// the codes never saturate.
+constexpr int VV8_ROWS_DMA = 80;                 // V^T rows streamed per block
+constexpr int VV8_PITCH = 64;                    // bytes per V^T row of a block
+constexpr int VT8_STAGE = VK_BYTES + VROWS * VV8_PITCH;
+
+__device__ __forceinline__ int key_of_row8(int row) {
+  const int kt = row >> 5, i = row & 31;
+  return 32 * ((i >> 2) & 1) + 16 * kt + 4 * (i >> 3) + (i & 3);
+}
+__device__ __forceinline__ int vswz8(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+
+template <int D, bool OUT_FP8>
+__global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
+    const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const uint8_t* __restrict__ vt,
+    int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale,
+    float v_scale) {
+  static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
+  constexpr int STAGES = 2;
+  constexpr int QWG = 4 * 32;                    // queries per workgroup
+  constexpr int NDC = D / 8;                     // 16-byte dim chunks per key (F16 K)
+  constexpr int NK = VK_BYTES / 1024;            // 1 KiB transfers for K per stage
+  constexpr int NV = VV8_ROWS_DMA * VV8_PITCH / 1024;  // 1 KiB transfers for V^T per stage
+  constexpr int NDMA = NK + NV;
+  constexpr int PER_WAVE = (NDMA + 3) / 4;
+  constexpr int RL = 8;                          // oacc[2] register holding O^T row 80 (lane group 0)
+  constexpr float kTau = 4.0f;                   // probabilities stay <= 2^4
+  constexpr float kPScale = 16.0f;               // P codes are e4m3(p * 2^4)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * VT8_STAGE + 1024];
+  uint8_t* trash = smem + STAGES * VT8_STAGE;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int fr = lane & 31;
+  const int fg = lane >> 5;
+  const int L = xcd_block(blockIdx.x, gridDim.x);
+  const int qb = L % nqb;
+  const int bh = L / nqb;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int hc = h * D;
+  const int64_t img = (int64_t)b * T;
+  const int qi = qb * QWG + wave * 32 + fr;
+  const uint8_t* vth = vt + (int64_t)bh * D * vt_ld;
+
+  f16x8 qf[5];
+#pragma unroll
+  for (int s = 0; s < 5; ++s) {
+    const int d0 = 16 * s + 8 * fg;
+    if (qi < T && d0 < D)
+      qf[s] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
+    else
+      qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  // constant V^T rows 80..95 of every stage: row 80 = e4m3(2^-exp), the rest 0
+  {
+    const uint32_t one = cvt_pk_e4m3(v_scale, v_scale, 0u, false) & 0xFFFF;
+    const uint32_t one4 = one | (one << 16);
+    constexpr int ZCH = (VROWS - VV8_ROWS_DMA) * VV8_PITCH / 16;
+    for (int i = t; i < STAGES * ZCH; i += 256) {
+      const int r = i % ZCH;
+      uint8_t* z = smem + (i / ZCH) * VT8_STAGE + VK_BYTES + VV8_ROWS_DMA * VV8_PITCH + r * 16;
+      *reinterpret_cast<i32x4*>(z) =
+          r < VV8_PITCH / 16 ? i32x4{(int)one4, (int)one4, (int)one4, (int)one4} : i32x4{0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  // transfer slots (slot j of this wave: global index jg = wave + 4 j); a
+  // V^T transfer fills 16 rows of 64 bytes, lane i row i / 4, physical
+  // chunk i % 4
+  const f16* ksrc[PER_WAVE];
+  const uint8_t* vsrc[PER_WAVE];
+  int kkey[PER_WAVE], kdc[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int jg = wave + 4 * j;
+    kkey[j] = 0;
+    kdc[j] = 0;
+    ksrc[j] = k + img * ld + hc;
+    vsrc[j] = vth;
+    if (jg < NK) {
+      const int off = jg * 1024 + 16 * lane;
+      kkey[j] = key_of_row8(off / VK_PITCH);
+      kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
+      ksrc[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
+    } else if (jg < NDMA) {
+      const int vr = 16 * (jg - NK) + (lane >> 2);
+      vsrc[j] = vth + (int64_t)vr * vt_ld + 16 * vswz8(vr, lane & 3);
+    }
+  }
+  auto issue = [&](int kb) {
+    const int key0 = kb * KB;
+    uint8_t* st = smem + (kb % STAGES) * VT8_STAGE;
+    const bool tail = key0 + KB > T;  // keys past T re-read token T-1
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int jg = wave + 4 * j;
+      if (jg < NK) {
+        const f16* p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
+                            : ksrc[j] + (int64_t)key0 * ld;
+        dma16(p, st + jg * 1024);
+      } else if (jg < NDMA) {
+        dma16(vsrc[j] + key0, st + VK_BYTES + (jg - NK) * 1024);
+      } else {
+        dma16(ksrc[0], trash);
+      }
+    }
+  };
+
+  const int koff = fr * VK_PITCH + fg * 16;
+  // V^T fragment of rows 32 dt + fr, key bytes 32 fg .. +31: chunks 2 fg, 2 fg + 1
+  int voff[3][2];
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int row = 32 * dt + fr;
+      voff[dt][h2] = VK_BYTES + row * VV8_PITCH + 16 * vswz8(row, 2 * fg + h2);
+    }
+
+  float m_run = kNegInf;
+  f32x16 oacc[3];
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
+
+  const int nkb = (T + KB - 1) / KB;
+  issue(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + 1 < nkb) issue(kb + 1);  // into the stage block kb-1 used
+    const uint8_t* st = smem + (kb % STAGES) * VT8_STAGE;
+    const int key0 = kb * KB;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
+      }
+    }
+    if (key0 + KB > T) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 32 * fg + 16 * kt + r >= T) sacc[kt][r] = kNegInf;
+    }
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      a[i] = fmaxf(fmaxf(sacc[0][i], sacc[0][i + 8]), fmaxf(sacc[1][i], sacc[1][i + 8]));
+    float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+    mx = half_swap_max(mx);
+    if (__any((mx - m_run) * c > kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+      for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+    // P^T fragment: byte 16 kt + r = e4m3(2^4 p) of key 32 fg + 16 kt + r
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kt = w >> 2, r0 = 4 * (w & 3);
+      float e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r0 + u], c, -mc)) * kPScale;
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
+      pf[w] = word;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 3; ++dt) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(st + voff[dt][0]);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(st + voff[dt][1]);
+      const i32x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, oacc[dt], 0, 0, 0, 127, 0, 127);
+    }
+  }
+
+  // the row sum sits in O^T row 80, register RL of lane group 0
+  const float lsum0 = oacc[2][RL];
+  const float lsum1 = half_other(lsum0);
+  if (qi >= T) return;
+  const float inv = 1.0f / (fg ? lsum1 : lsum0);
+#pragma unroll
+  for (int dt = 0; dt < 3; ++dt)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      const int d0 = 32 * dt + 8 * qd + 4 * fg;
+      if (d0 >= D) continue;
+      const float a0 = oacc[dt][4 * qd + 0] * inv, a1 = oacc[dt][4 * qd + 1] * inv;
+      const float a2 = oacc[dt][4 * qd + 2] * inv, a3 = oacc[dt][4 * qd + 3] * inv;
+      if constexpr (OUT_FP8) {
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(o) + (img + qi) * ldo + hc + d0) =
+            pack4_e4m3(a0 * out_scale, a1 * out_scale, a2 * out_scale, a3 * out_scale);
+      } else {
+        const f16x4 ov = {(f16)a0, (f16)a1, (f16)a2, (f16)a3};
+        *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(o) + (img + qi) * ldo + hc + d0) = ov;
+      }
+    }
+}
+
 template <int D>
 hipError_t launch_vt_d(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o, int64_t ldo,
                        int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale, hipStream_t s) {
@@ -655,6 +898,41 @@ hipError_t launch_flash_attention_vt(const f16* q, const f16* k, int64_t ld, con
     case 64: return launch_vt_d<64>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
     case 72: return launch_vt_d<72>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
     case 80: return launch_vt_d<80>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+namespace {
+template <int D>
+hipError_t launch_vt8_d(const f16* q, const f16* k, int64_t ld, const uint8_t* vt, int64_t vt_ld, void* o,
+                        int64_t ldo, int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale,
+                        float v_scale, hipStream_t s) {
+  const int nqb = (tokens + QB - 1) / QB;
+  const int64_t blocks = (int64_t)nqb * heads * batch;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (out_fp8)
+    hipLaunchKernelGGL((flash_attn_vt8_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt, vt_ld,
+                       o, ldo, tokens, heads, nqb, sl2, out_scale, v_scale);
+  else
+    hipLaunchKernelGGL((flash_attn_vt8_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt,
+                       vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale, v_scale);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_flash_attention_vt8(const f16* q, const f16* k, int64_t ld, const uint8_t* vt, int64_t vt_ld,
+                                      void* o, int64_t ldo, int batch, int heads, int tokens, int head_dim,
+                                      float scale, bool out_fp8, float out_scale, float v_scale, hipStream_t s) {
+  if (batch < 1 || heads < 1 || tokens < 1 || !flash_attention_vt_supported(head_dim) ||
+      ld < (int64_t)heads * head_dim || (ld & 7) || ldo < (int64_t)heads * head_dim || (ldo & 3) ||
+      vt_ld < (int64_t)(tokens + KB - 1) / KB * KB || (vt_ld & 15) ||
+      (reinterpret_cast<uintptr_t>(vt) & 15) || !(v_scale > 0.0f) || v_scale > 256.0f)
+    return hipErrorInvalidValue;
+  const float sl2 = scale * 1.4426950408889634f;
+  switch (head_dim) {
+    case 64: return launch_vt8_d<64>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 72: return launch_vt8_d<72>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 80: return launch_vt8_d<80>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
   }
   return hipErrorInvalidValue;
 }

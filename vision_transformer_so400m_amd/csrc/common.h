@@ -92,7 +92,8 @@ enum GemmEpi : int {
   EPI_BIAS_RES = 2,  // acc*s + bias[n] + res[m][n]
   EPI_BIAS_GELU = 3, // gelu(acc*s + bias[n])
   EPI_QKV = 4        // acc*s + bias[n]; columns >= vt_col0 (the V part) go to
-                     // vt transposed per head instead of to c
+                     // vt transposed per head instead of to c (as F16, or as
+                     // e4m3 codes of value*out_scale when out_fp8 is set)
 };
 
 struct GemmArgs {
@@ -106,7 +107,8 @@ struct GemmArgs {
   float acc_scale;                // 1 (F16) or 2^(2*exp) (FP8)
   float out_scale;                // for e4m3 outputs: 2^-exp
   // EPI_QKV: V^T[(b*vt_heads + h)*vt_dim + d][t] at vt + row*vt_ld + t, for
-  // output row m = b*vt_tokens + t and column vt_col0 + h*vt_dim + d
+  // output row m = b*vt_tokens + t and column vt_col0 + h*vt_dim + d; vt and
+  // vt_ld count elements of the V^T type (F16, or bytes for e4m3)
   f16* vt; int vt_col0, vt_tokens, vt_heads, vt_dim; int64_t vt_ld;
   float vt_inv_dim;  // 1 / vt_dim
   int group_m;       // tile-order band height in row blocks (<= 0: N-fastest)
@@ -136,6 +138,15 @@ hipError_t launch_flash_attention_vt(const f16* q, const f16* k, int64_t ld, con
                                      void* o, int64_t ldo, int batch, int heads, int tokens,
                                      int head_dim, float scale, bool out_fp8, float out_scale,
                                      hipStream_t s);
+
+// The same with the PV product in e4m3: vt holds codes of v * v_scale (bytes,
+// row stride vt_ld, a multiple of 16, zero codes in columns tokens..vt_ld-1;
+// the 80 - head_dim rows after the last head's must be readable), the
+// probabilities are quantized to e4m3(p * 2^4) in registers. v_scale is a
+// power of two in (0, 256].
+hipError_t launch_flash_attention_vt8(const f16* q, const f16* k, int64_t ld, const uint8_t* vt, int64_t vt_ld,
+                                      void* o, int64_t ldo, int batch, int heads, int tokens, int head_dim,
+                                      float scale, bool out_fp8, float out_scale, float v_scale, hipStream_t s);
 bool flash_attention_vt_supported(int head_dim);
 
 hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv,
@@ -176,6 +187,8 @@ hipError_t launch_f32_convert(const float* x, int rows, int cols, void* y,
 
 // Zero columns c0..c1-1 of every row of an F16 [rows, ld] matrix.
 hipError_t launch_zero_cols(f16* p, int64_t rows, int64_t ld, int c0, int c1, hipStream_t s);
+// The same for a byte matrix (e4m3 codes): columns [c0, c1) of rows rows.
+hipError_t launch_zero_cols_u8(uint8_t* p, int64_t rows, int64_t ld, int c0, int c1, hipStream_t s);
 
 // Fill n 16-bit words.
 hipError_t launch_fill_u16(void* p, size_t n, uint16_t value, hipStream_t s);

@@ -94,6 +94,13 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(f16* __restrict__ p, int
   p[(i / w) * ld + c0 + (i % w)] = (f16)0.0f;
 }
 
+__global__ __launch_bounds__(256) void zero_cols_u8_kernel(uint8_t* __restrict__ p, int64_t rows, int64_t ld, int c0,
+                                                           int w) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * w) return;
+  p[(i / w) * ld + c0 + (i % w)] = 0;  // e4m3 code of +0
+}
+
 __global__ __launch_bounds__(256) void fill_u16_kernel(uint16_t* __restrict__ p, size_t n, uint16_t v) {
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -143,6 +150,14 @@ hipError_t launch_zero_cols(f16* p, int64_t rows, int64_t ld, int c0, int c1, hi
   const int64_t n = rows * (c1 - c0);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(zero_cols_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, rows, ld, c0, c1 - c0);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_cols_u8(uint8_t* p, int64_t rows, int64_t ld, int c0, int c1, hipStream_t s) {
+  if (rows < 0 || c0 < 0 || c1 > ld || c1 < c0) return hipErrorInvalidValue;
+  const int64_t n = rows * (c1 - c0);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_cols_u8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, rows, ld, c0, c1 - c0);
   return hipGetLastError();
 }
 

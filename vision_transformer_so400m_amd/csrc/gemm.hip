@@ -57,11 +57,13 @@ __device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3)
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
 
 // Element type of the output tile staged in LDS: F32 while a residual is
-// still to be added (one rounding), else the output type.
+// still to be added (one rounding), else the output type (for EPI_QKV the Q
+// and K columns are F16 either way; OUT_FP8 there makes V^T e4m3).
 template <int EPI, bool OUT_FP8>
 struct StageType {
-  typedef typename std::conditional<EPI == EPI_BIAS_RES, float,
-                                    typename std::conditional<OUT_FP8, uint8_t, f16>::type>::type type;
+  typedef typename std::conditional<
+      EPI == EPI_BIAS_RES, float,
+      typename std::conditional<OUT_FP8 && EPI != EPI_QKV, uint8_t, f16>::type>::type type;
 };
 
 // Linear workgroup id -> output tile. Workgroups are dispatched round-robin
@@ -236,14 +238,15 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
     if (n0 + wn * WN >= g.vt_col0) {
       // V columns (whole waves: vt_col0 is a multiple of 128): 4 consecutive
       // dims of one head written transposed. The 32 lanes of a half-wave hold
-      // 32 consecutive tokens, so each store covers 64 contiguous bytes of a
-      // V^T row.
+      // 32 consecutive tokens, so each store covers 64 (F16) or 32 (e4m3)
+      // contiguous bytes of a V^T row.
+      using VT = typename std::conditional<OUT_FP8, uint8_t, f16>::type;
 #pragma unroll
       for (int i = 0; i < T::TM; ++i) {
         const int m = m0 + wm * WM + i * 32 + fr;
         if (m >= g.M) continue;
         const int bb = m / g.vt_tokens, tt = m - bb * g.vt_tokens;
-        f16* vrow0 = g.vt + (int64_t)bb * g.vt_heads * g.vt_dim * g.vt_ld + tt;
+        VT* vrow0 = reinterpret_cast<VT*>(g.vt) + (int64_t)bb * g.vt_heads * g.vt_dim * g.vt_ld + tt;
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
 #pragma unroll
@@ -253,9 +256,15 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
             const int hd = n - g.vt_col0;  // head*dim + d; the 4 dims never cross a head (dim % 4 == 0)
             const int hh = (int)(((float)hd + 0.5f) * g.vt_inv_dim);  // exact: hd < 2^20, dim <= 2^10
             const int dd = hd - hh * g.vt_dim;
-            f16* dst = vrow0 + ((int64_t)hh * g.vt_dim + dd) * g.vt_ld;
+            VT* dst = vrow0 + ((int64_t)hh * g.vt_dim + dd) * g.vt_ld;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[r * g.vt_ld] = (f16)(acc[i][j][4 * qq + r] * g.acc_scale + bv[r]);
+            for (int r = 0; r < 4; ++r) {
+              const float v = acc[i][j][4 * qq + r] * g.acc_scale + bv[r];
+              if constexpr (OUT_FP8)
+                dst[r * g.vt_ld] = (uint8_t)(cvt_pk_e4m3(v * g.out_scale, 0.f, 0u, false) & 0xFF);
+              else
+                dst[r * g.vt_ld] = (f16)v;
+            }
           }
         }
       }
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
     }
   }
   __syncthreads();
-  constexpr int OB = OUT_FP8 ? 1 : 2;
+  constexpr int OB = SB == 1 ? 1 : 2;
   constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
   constexpr int VPC = 16 / OB;       // values per output chunk
 #pragma unroll 4
@@ -392,7 +401,8 @@ hipError_t launch_epi(const GemmArgs& g, int epi, bool out_fp8, hipStream_t s) {
     case EPI_BIAS: return launch_sized<FP8, EPI_BIAS, false>(g, s);
     case EPI_BIAS_POS: return launch_sized<FP8, EPI_BIAS_POS, false>(g, s);
     case EPI_BIAS_RES: return launch_sized<FP8, EPI_BIAS_RES, false>(g, s);
-    case EPI_QKV: return launch_sized<FP8, EPI_QKV, false>(g, s);
+    case EPI_QKV:
+      return out_fp8 ? launch_sized<FP8, EPI_QKV, true>(g, s) : launch_sized<FP8, EPI_QKV, false>(g, s);
     case EPI_BIAS_GELU:
       return out_fp8 ? launch_sized<FP8, EPI_BIAS_GELU, true>(g, s)
                      : launch_sized<FP8, EPI_BIAS_GELU, false>(g, s);
@@ -410,9 +420,10 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   if (g.lda < g.K || g.ldw < g.K || g.ldc < g.N) return hipErrorInvalidValue;
   if ((int64_t)g.M * g.lda * E >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
-  if (out_fp8 && epi != EPI_BIAS_GELU) return hipErrorInvalidValue;
+  // e4m3 output: the GELU epilogue's output, or V^T of the QKV epilogue
+  if (out_fp8 && epi != EPI_BIAS_GELU && epi != EPI_QKV) return hipErrorInvalidValue;
   // 16-byte transfers: operand rows, output rows and residual rows aligned
-  const int OB = out_fp8 ? 1 : 2;
+  const int OB = (out_fp8 && epi != EPI_QKV) ? 1 : 2;
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
   if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * E) % 16 || (g.ldw * E) % 16 ||
       (g.ldc * OB) % 16)

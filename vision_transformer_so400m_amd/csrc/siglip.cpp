@@ -117,6 +117,8 @@ struct siglip_model {
   float acc_scale = 1.0f;  // product rescale 2^(2 exp)
   int patch_pad = 0, mlp_pad = 0;
   bool vt_path = false;  // V written transposed by the QKV GEMM for the streaming attention
+  bool attn_fp8 = false; // PV product in e4m3: V^T as e4m3 codes of v * attn_v_scale
+  float attn_v_scale = 1.0f;
   int tokens_pad = 0;    // V^T row length: tokens rounded up to the 64-key block
 
   std::vector<void*> allocs;
@@ -295,7 +297,7 @@ struct Acts {
   f16* my;
   void* ma;
   void* mu;
-  f16* vt;
+  void* vt;  // F16, or e4m3 codes with attention_fp8
   float* mscores;
   float* zbar;
 };
@@ -315,7 +317,7 @@ Acts acts_at(const siglip_model* m, int b0) {
   A.my = m->my + b0 * W;
   A.ma = at(m->ma, b0 * W * es);
   A.mu = at(m->mu, b0 * m->mlp_pad * es);
-  A.vt = m->vt ? m->vt + (int64_t)b0 * W * m->tokens_pad : nullptr;
+  A.vt = at(m->vt, (int64_t)b0 * W * m->tokens_pad * (m->attn_fp8 ? 1 : 2));
   A.mscores = m->mscores ? m->mscores + r0 * 16 : nullptr;
   A.zbar = m->zbar ? m->zbar + (int64_t)b0 * 16 * W : nullptr;
   return A;
@@ -346,7 +348,7 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
 
 // The fused QKV projection: Q and K row-major into qkv, V transposed per
 // head into vt when the streaming attention is used.
-void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, f16* vt, int M, hipStream_t s) {
+void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* vt, int M, hipStream_t s) {
   const Gemm& g = Ly.qkv;
   if (m->separate_qkv) {
     // Q and K into their columns of the fused row; V as its own projection,
@@ -370,15 +372,15 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, f16* vt
     args.N = Ly.v.n_pad;
     args.K = Ly.v.k_pad;
     args.acc_scale = m->acc_scale;
-    args.out_scale = m->op_scale;
-    args.vt = vt;
+    args.out_scale = m->attn_fp8 ? m->attn_v_scale : m->op_scale;
+    args.vt = static_cast<f16*>(vt);
     args.vt_col0 = 0;
     args.vt_tokens = m->tokens;
     args.vt_heads = m->heads;
     args.vt_dim = m->head_dim;
     args.vt_ld = m->tokens_pad;
     args.vt_inv_dim = 1.0f / (float)m->head_dim;
-    hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "v gemm launch");
+    hip_check(launch_gemm(args, EPI_QKV, m->fp8, m->attn_fp8, s), "v gemm launch");
     return;
   }
   if (!m->vt_path) {
@@ -397,8 +399,8 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, f16* vt
   args.N = g.n_pad;
   args.K = g.k_pad;
   args.acc_scale = m->acc_scale;
-  args.out_scale = m->op_scale;
-  args.vt = vt;
+  args.out_scale = m->attn_fp8 ? m->attn_v_scale : m->op_scale;
+  args.vt = static_cast<f16*>(vt);
   args.vt_col0 = 2 * m->width;
   args.vt_tokens = m->tokens;
   args.vt_heads = m->heads;
@@ -409,7 +411,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, f16* vt
   // activations: walk tiles in bands of 8 row blocks (measured ~12% faster
   // at 46,656 rows than row-block-major order)
   args.group_m = 8;
-  hip_check(launch_gemm(args, EPI_QKV, m->fp8, false, s), "qkv gemm launch");
+  hip_check(launch_gemm(args, EPI_QKV, m->fp8, m->attn_fp8, s), "qkv gemm launch");
 }
 
 void capture(siglip_model* m, int stage, const void* src, size_t bytes, hipStream_t s) {
@@ -432,6 +434,7 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
       r = m->vt_path ? (int64_t)batch * m->heads * m->head_dim : 0;
       c = m->tokens;
       l = m->tokens_pad;
+      b = m->attn_fp8 ? 1 : 2;
       break;
     case SIGLIP_STAGE_MLP_HIDDEN: c = m->mlp; l = m->mlp_pad; b = e; break;
     case SIGLIP_STAGE_MAP_KV: c = l = 2LL * m->width; r = m->map_fold ? 0 : M; break;
@@ -502,8 +505,13 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
   if (m->vt_path && m->tokens_pad > m->tokens) {
     // V^T columns past the last token are read by the last key block: zeros
     LaunchTimer lt(m, SIGLIP_K_INPUT, s);
-    hip_check(launch_zero_cols(A.vt, (int64_t)B * m->heads * m->head_dim, m->tokens_pad, m->tokens, m->tokens_pad, s),
-              "zero V^T tail");
+    const int64_t vrows = (int64_t)B * m->heads * m->head_dim;
+    if (m->attn_fp8)
+      hip_check(launch_zero_cols_u8(static_cast<uint8_t*>(A.vt), vrows, m->tokens_pad, m->tokens, m->tokens_pad, s),
+                "zero V^T tail");
+    else
+      hip_check(launch_zero_cols(static_cast<f16*>(A.vt), vrows, m->tokens_pad, m->tokens, m->tokens_pad, s),
+                "zero V^T tail");
   }
   if (cap) capture(m, SIGLIP_STAGE_EMBED, A.h, cb(SIGLIP_STAGE_EMBED), s);
 
@@ -524,9 +532,15 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
     if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, A.vt, cb(SIGLIP_STAGE_V_T), s);
     {
       LaunchTimer lt(m, SIGLIP_K_ATTENTION, s);
-      if (m->vt_path)
-        hip_check(launch_flash_attention_vt(A.qkv, A.qkv + W, 3 * W, A.vt, m->tokens_pad, A.o, W, B, m->heads,
-                                            m->tokens, m->head_dim, attn_scale, q8, m->op_scale, s),
+      if (m->attn_fp8)
+        hip_check(launch_flash_attention_vt8(A.qkv, A.qkv + W, 3 * W, static_cast<const uint8_t*>(A.vt),
+                                             m->tokens_pad, A.o, W, B, m->heads, m->tokens, m->head_dim,
+                                             attn_scale, q8, m->op_scale, m->attn_v_scale, s),
+                  "attention");
+      else if (m->vt_path)
+        hip_check(launch_flash_attention_vt(A.qkv, A.qkv + W, 3 * W, static_cast<const f16*>(A.vt), m->tokens_pad,
+                                            A.o, W, B, m->heads, m->tokens, m->head_dim, attn_scale, q8,
+                                            m->op_scale, s),
                   "attention");
       else
         hip_check(launch_flash_attention(A.qkv, A.qkv + W, A.qkv + 2 * W, 3 * W, A.o, W, B, m->heads, m->tokens,
@@ -689,6 +703,10 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_INVALID_ARG, "separate_qkv must be 0 or 1");
   if (opt->map_explicit_kv != 0 && opt->map_explicit_kv != 1)
     return fail(SIGLIP_E_INVALID_ARG, "map_explicit_kv must be 0 or 1");
+  if (opt->attention_fp8 != 0 && opt->attention_fp8 != 1)
+    return fail(SIGLIP_E_INVALID_ARG, "attention_fp8 must be 0 or 1");
+  if (opt->attention_fp8 == 1 && (opt->fp8_scale_exp < -8 || opt->fp8_scale_exp > 8))
+    return fail(SIGLIP_E_INVALID_ARG, "fp8_scale_exp must be in -8..8");
   if (blob_bytes < sizeof(BlobHeader)) return fail(SIGLIP_E_BAD_BLOB, "blob shorter than its 64-byte header");
   BlobHeader h;
   std::memcpy(&h, blob, sizeof h);
@@ -780,6 +798,12 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->vt_path = flash_attention_vt_supported(m->head_dim);
     m->tokens_pad = (int)round_up(T, 64);
     m->separate_qkv = opt->separate_qkv == 1;
+    m->attn_fp8 = opt->attention_fp8 == 1;
+    if (m->attn_fp8 && !m->vt_path) {
+      delete m;
+      return fail(SIGLIP_E_UNSUPPORTED, "attention_fp8 needs head_dim 64, 72 or 80");
+    }
+    m->attn_v_scale = std::ldexp(1.0f, -opt->fp8_scale_exp);
     m->map_fold = opt->map_explicit_kv == 0 && map_fold_supported(W, m->heads, m->head_dim, T);
 
     const size_t staging_floats = (size_t)std::max<int64_t>({(int64_t)P * W, 3LL * W * W, (int64_t)W * F, (int64_t)T * W});
@@ -834,6 +858,9 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
         {&m->xp, M * m->patch_pad * es}, {(void**)&m->h, M * W * 2}, {&m->a, M * W * es},
         {(void**)&m->qkv, M * 3 * W * 2}, {&m->o, M * W * es}, {&m->u, M * m->mlp_pad * es},
         {&m->mo, B * W * es}, {(void**)&m->my, B * W * 2}, {&m->ma, B * W * es}, {&m->mu, B * m->mlp_pad * es},
+        // V^T at F16 size in both modes: with e4m3 codes the unused half is the
+        // slack that the e4m3 attention kernel's reads of rows D..79 past the
+        // last head land in
         {(void**)&m->vt, m->vt_path ? B * W * m->tokens_pad * 2 : 0},
         {(void**)&m->mscores, m->map_fold ? M * 16 * 4 : 0},
         {(void**)&m->zbar, m->map_fold ? B * 16 * W * 4 : 0},
