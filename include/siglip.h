@@ -141,7 +141,11 @@ SIGLIP_API int siglip_create(const void* blob, size_t blob_bytes,
  * on hip_stream alone.
  * The model's workspace is shared by its calls: calls on one model must be
  * ordered (one stream, or explicit synchronisation). Results are bitwise
- * deterministic run to run. Errors: INVALID_ARG, HIP.
+ * deterministic run to run. The call enqueues kernel launches and event
+ * records/waits only (no allocation, memset or host synchronisation), so it
+ * may be captured into a HIP graph by stream capture on hip_stream and the
+ * graph replayed; a replay reads and writes the pointers given at capture.
+ * Errors: INVALID_ARG, HIP.
  */
 SIGLIP_API int siglip_encode(siglip_model* m, const void* pixels_f16,
                              int32_t batch, void* out_f16, void* hip_stream);

@@ -498,6 +498,38 @@ def test_half_batch_streams_match_one_stream_bitwise(V, fp8):
         assert torch.equal(bits, one.view(torch.int16)), b
 
 
+@pytest.mark.parametrize("batch", [1, 3], ids=["b1", "b3_two_streams"])
+def test_graph_capture_replays_match_eager(V, batch):
+    """siglip_encode enqueues only kernels and event waits (no allocation,
+    memset or host synchronization), so a caller can capture it into a HIP
+    graph. Every replay, with other eager calls on the same workspace and host
+    synchronizations between the replays, must give the eager call's bits;
+    batch 3 captures the fork to the model's second stream and the join."""
+    dims = S.SO400M.with_depth(2)
+    _flush(f"graph capture batch={batch}")
+    model, _ = make_model(V, dims, 7, max_batch=4, fp8=True)
+    x = torch.from_numpy(S.make_pixels(dims, batch, 8)).cuda()
+    x2 = torch.from_numpy(S.make_pixels(dims, 4, 9)).cuda()
+    eager = model.encode(x).clone()
+    other = model.encode(x2).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        model.encode(x, out=out, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(float("nan"))
+        y2 = model.encode(x2)
+        torch.cuda.synchronize()
+        assert torch.equal(y2.view(torch.int16), other.view(torch.int16)), r
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), r
+    del g
+    model.close()
+
+
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
 def test_separate_qkv_matches_fused_bitwise(V, fp8):
     """Separate Q/K/V (and MAP K/V) projections against the fused ones: every

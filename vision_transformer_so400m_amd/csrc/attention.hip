@@ -573,7 +573,6 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
   constexpr int PER_WAVE = (NDMA + 3) / 4;
   constexpr int RL = 8;                          // oacc[2] register holding O^T row 80 (lane group 0)
   constexpr float kTau = 4.0f;                   // probabilities stay <= 2^4
-  constexpr float kPScale = 16.0f;               // P codes are e4m3(p * 2^4)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * VT8_STAGE + 1024];
   uint8_t* trash = smem + STAGES * VT8_STAGE;
 
@@ -718,7 +717,8 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       m_run = m_new;
     }
-    const float mc = m_run * c;
+    // 2^4 p = exp2(s c - (m_run c - 4)): the code scale rides in the exponent
+    const float mc = fmaf(m_run, c, -4.0f);
     // P^T fragment: byte 16 kt + r = e4m3(2^4 p) of key 32 fg + 16 kt + r
     i32x8 pf;
 #pragma unroll
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
       const int kt = w >> 2, r0 = 4 * (w & 3);
       float e[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r0 + u], c, -mc)) * kPScale;
+      for (int u = 0; u < 4; ++u) e[u] = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r0 + u], c, -mc));
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], word, true);
       pf[w] = word;
