@@ -469,6 +469,16 @@ def test_determinism_and_nan_poisoned_workspace(V):
     b = model8.encode(xt).cpu().numpy()
     np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
     assert np.isfinite(a).all()
+    # e4m3 PV attention: 0x7F7F is a NaN in F16 and, byte by byte, in e4m3, so
+    # the V^T rows past each head's 72 that the kernel reads (and the slack
+    # after the last head) hold NaN codes; they must not reach the output
+    model8p, _ = make_model(V, dims, 0, max_batch=3, fp8=True, attention_fp8=True)
+    model8p.debug_fill_workspace(0)
+    a = model8p.encode(xt).cpu().numpy()
+    model8p.debug_fill_workspace(0x7F7F)
+    b = model8p.encode(xt).cpu().numpy()
+    np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.isfinite(a).all()
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
@@ -530,21 +540,23 @@ def test_graph_capture_replays_match_eager(V, batch):
     model.close()
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
-def test_separate_qkv_matches_fused_bitwise(V, fp8):
+@pytest.mark.parametrize("fp8,attn_fp8", [(False, False), (True, False), (True, True)],
+                         ids=["f16", "fp8", "fp8_e4m3_pv"])
+def test_separate_qkv_matches_fused_bitwise(V, fp8, attn_fp8):
     """Separate Q/K/V (and MAP K/V) projections against the fused ones: every
     output element has the same operands and summation order, so results are
     identical, at batch 2 (small tiles) and batch 64 (the large-batch tile
-    shapes, where the fused and separate widths take different tiles)."""
+    shapes, where the fused and separate widths take different tiles); with
+    e4m3 PV attention the separate V projection writes the e4m3 V^T codes."""
     dims = S.SO400M.with_depth(2)
     wt = S.make_weights(dims, 3)
     blob = S.pack_blob(dims, wt)
     del wt
     for b in (2, 64):
-        _flush(f"separate vs fused QKV, fp8={fp8}, B={b}")
+        _flush(f"separate vs fused QKV, fp8={fp8}, attention_fp8={attn_fp8}, B={b}")
         x = torch.from_numpy(S.make_pixels(dims, b, 3)).cuda()
-        fused = V.Model(blob, max_batch=b, fp8=fp8, map_explicit_kv=True)
-        sep = V.Model(blob, max_batch=b, fp8=fp8, separate_qkv=True, map_explicit_kv=True)
+        fused = V.Model(blob, max_batch=b, fp8=fp8, map_explicit_kv=True, attention_fp8=attn_fp8)
+        sep = V.Model(blob, max_batch=b, fp8=fp8, separate_qkv=True, map_explicit_kv=True, attention_fp8=attn_fp8)
         fused.debug_capture(1)
         sep.debug_capture(1)
         yf = fused.encode(x)
