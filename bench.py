@@ -131,8 +131,8 @@ def sweep(args):
     images/s at B = 1..64 for e4m3 and F16 GEMM operands; the projected-
     attention block (LN + QKV + attention + out-proj) and the MLP block
     (LN + up + down) from per-launch HIP events at B = 1 and B = 64; fused
-    against separate Q/K/V projections; F16 against e4m3 PV attention
-    products."""
+    against separate Q/K/V projections; F16 against e4m3 attention products
+    (PV, QK, both)."""
     import torch
 
     import synthetic as S
@@ -178,9 +178,9 @@ def sweep(args):
             res["qkv_projections"][tag][f"b{b}"] = {"ms": round(ms, 4), "qkv_us_per_layer": round(qkv_us, 2),
                                                     "map_kv_us": round(ct["MAP_KV"][0] * ct["MAP_KV"][1], 2)}
         model.close()
-    for afp8 in (False, True):
+    for afp8 in (0, 1, 2, 3):
         model = V.Model(blob, max_batch=64, fp8=True, attention_fp8=afp8)
-        tag = "e4m3_pv" if afp8 else "f16"
+        tag = ("f16", "e4m3_pv", "e4m3_qk", "e4m3_qk_pv")[afp8]
         res["attention_products"][tag] = {}
         for b in (1, 64):
             x = xall[:b].contiguous()

@@ -76,15 +76,17 @@ typedef struct {
    * 1 = the explicit K/V projection of every token (an e4m3 GEMM in FP8
    * mode) followed by the probe attention. */
   int32_t map_explicit_kv;
-  /* 0 = F16 attention products (the default); 1 = the encoder attention's
-   * PV product in OCP e4m3 (page "FP8 attention and resident image/embedding
-   * transfers": F143 operands at scale -4 for PV, softmax state and the
-   * attention output precision unchanged). The QKV projection writes V^T as
-   * e4m3 codes of v * 2^-fp8_scale_exp and the probabilities are quantized
-   * to e4m3(p * 2^4) in registers, so no separate cast runs (the same page,
-   * "Full 27-layer ViT": producer-written operands). The QK product stays
-   * F16. Independent of gemm_precision; needs head_dim 64, 72 or 80
-   * (UNSUPPORTED otherwise). fp8_scale_exp must then be in -8..8. */
+  /* Encoder attention products in OCP e4m3 (page "FP8 attention and
+   * resident image/embedding transfers": F143 operands at scale -4, PV and
+   * QK selected independently, softmax state and the attention output
+   * precision unchanged). 0 = both F16 (the default). Bit 0 (1) = PV: the
+   * QKV projection writes V^T as e4m3 codes of v * 2^-fp8_scale_exp and the
+   * probabilities are quantized to e4m3(p * 2^4) in registers. Bit 1 (2) =
+   * QK: the QKV projection writes Q and K as e4m3 codes of x *
+   * 2^-fp8_scale_exp. 3 = both. No separate cast runs (the same page, "Full
+   * 27-layer ViT": producer-written operands). Independent of
+   * gemm_precision; needs head_dim 64, 72 or 80 (UNSUPPORTED otherwise).
+   * fp8_scale_exp must then be in -8..8. */
   int32_t attention_fp8;
 } siglip_options;
 
@@ -218,10 +220,14 @@ typedef enum {
   SIGLIP_STAGE_MAP_Q = 14,     /* [1, width]   F16  probe query (create time) */
   SIGLIP_STAGE_V_T = 15,       /* [B*heads*head_dim, round_up(tokens,64)] F16
                                   (e4m3 codes of v * 2^-fp8_scale_exp with
-                                  attention_fp8): V of each (image, head)
-                                  transposed (dims x tokens, zeros past
+                                  the e4m3 PV product): V of each (image,
+                                  head) transposed (dims x tokens, zeros past
                                   tokens); when present, the QKV stage holds
-                                  only the Q and K columns                    */
+                                  only the Q and K columns; with the e4m3 QK
+                                  product the QKV stage is [M, 2*heads*80]
+                                  e4m3 codes, head slots of 80 bytes (Q heads,
+                                  then K heads; bytes head_dim..79 of a slot
+                                  unused), row stride 6*width bytes           */
   SIGLIP_STAGE_COUNT = 16
 } siglip_stage;
 

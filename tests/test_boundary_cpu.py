@@ -137,15 +137,17 @@ def test_bad_map_explicit_kv_value(blob1):
 def test_bad_attention_fp8_value(blob1):
     lib = V.load_library()
     out = ctypes.c_void_p()
-    opt = V.siglip_options(0, 1, 0, -4, 0, 0, 2)
-    st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
-    assert st == V.SIGLIP_E_INVALID_ARG and not out.value
-    assert b"attention_fp8" in lib.siglip_last_error()
-    # its scale exponent is checked even with F16 GEMM operands
-    opt = V.siglip_options(0, 1, 0, 9, 0, 0, 1)
-    st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
-    assert st == V.SIGLIP_E_INVALID_ARG and not out.value
-    assert b"fp8_scale_exp" in lib.siglip_last_error()
+    for bad in (4, -1):  # bits 0 (PV) and 1 (QK) only
+        opt = V.siglip_options(0, 1, 0, -4, 0, 0, bad)
+        st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
+        assert st == V.SIGLIP_E_INVALID_ARG and not out.value
+        assert b"attention_fp8" in lib.siglip_last_error()
+    # its scale exponent is checked even with F16 GEMM operands, for either product
+    for mode in (1, 2, 3):
+        opt = V.siglip_options(0, 1, 0, 9, 0, 0, mode)
+        st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
+        assert st == V.SIGLIP_E_INVALID_ARG and not out.value
+        assert b"fp8_scale_exp" in lib.siglip_last_error()
 
 
 def test_unsupported_width_is_reported_before_the_device():

@@ -247,8 +247,11 @@ def _dec(model, arr, fp8):
     return arr.astype(np.float64)
 
 
-def check_stages(model, wt, x, dims, fp8, batch, attn_fp8=False):
-    """Every captured stage of layer 0 against the oracle on the GPU's inputs."""
+def check_stages(model, wt, x, dims, fp8, batch, attn_fp8=0):
+    """Every captured stage of layer 0 against the oracle on the GPU's inputs.
+    attn_fp8: e4m3 attention products (1 = PV, 2 = QK, 3 = both)."""
+    attn_fp8 = 1 if attn_fp8 is True else int(attn_fp8)
+    pv8, qk8 = bool(attn_fp8 & 1), bool(attn_fp8 & 2)
     se = model.fp8_scale_exp
     M, W, T, F, H, D = batch * dims.tokens, dims.width, dims.tokens, dims.mlp, dims.heads, dims.head_dim
     st = {n: _stage(model, n) for n in
@@ -289,30 +292,42 @@ def check_stages(model, wt, x, dims, fp8, batch, attn_fp8=False):
     pos = np.tile(wt["pos"].astype(np.float64), (batch, 1))
     gemm_check("EMBED", xin, "embed.w", "embed.b", add=pos)
     ln_check("LN1", f("EMBED"), "layer0.ln1")
-    qk_cols = st["QKV"].shape[1]
-    gemm_check("QKV", f("LN1"), "layer0.qkv.w", "layer0.qkv.b", cols=qk_cols)
+    if qk8:
+        # Q then K as e4m3 codes of x * 2^-fp8_scale_exp in head slots of 80 bytes
+        slots = st["QKV"]
+        assert slots.dtype == np.uint8 and slots.shape == (M, 2 * H * 80)
+        st["QKV"] = np.ascontiguousarray(slots.reshape(M, 2 * H, 80)[:, :, :D].reshape(M, 2 * W))
+        w_qk = dw("layer0.qkv.w")[:, :2 * W]
+        ref_qk = O.linear(f("LN1"), w_qk, wt["layer0.qkv.b"][:2 * W].astype(np.float64))
+        e4m3_neighbours_ok("QKV (Q, K e4m3)", st["QKV"], ref_qk, se, band=acc_tol(f("LN1"), w_qk) + 1e-6)
+        qk_vals = _dec(model, st["QKV"], True)
+        qk_cols = 2 * W
+    else:
+        qk_cols = st["QKV"].shape[1]
+        gemm_check("QKV", f("LN1"), "layer0.qkv.w", "layer0.qkv.b", cols=qk_cols)
+        qk_vals = f("QKV")
     if qk_cols == 2 * W:
         # V arrives transposed per head: rows (b*H + h)*D + d, tokens padded with zeros
         vt_full = model.debug_stage("V_T", full=True)
         assert vt_full.shape[0] == batch * H * D and vt_full.shape[1] >= T and vt_full.shape[1] % 64 == 0
-        assert vt_full.dtype == (np.uint8 if attn_fp8 else np.float16)
+        assert vt_full.dtype == (np.uint8 if pv8 else np.float16)
         assert not vt_full[:, T:].view(np.uint8).any(), "V^T padding must be exact zeros"
         v_gpu = vt_full[:, :T].reshape(batch, H, D, T).transpose(0, 3, 1, 2).reshape(M, W)
         st["V_FROM_VT"] = v_gpu
         w = dw("layer0.qkv.w")[:, 2 * W:]
         ref_v = O.linear(f("LN1"), w, wt["layer0.qkv.b"][2 * W:].astype(np.float64))
-        if attn_fp8:
+        if pv8:
             # e4m3 codes of v * 2^-fp8_scale_exp, nearest to the exact product
             e4m3_neighbours_ok("V (from V^T, e4m3)", v_gpu, ref_v, se, band=acc_tol(f("LN1"), w) + 1e-6)
             v_gpu = _dec(model, v_gpu, True)
         else:
             assert_close("V (from V^T)", v_gpu, ref_v, extra=acc_tol(f("LN1"), w) + 1e-6)
-        qkv = np.concatenate([f("QKV"), v_gpu.astype(np.float64)], axis=1).reshape(batch, T, 3 * W)
+        qkv = np.concatenate([qk_vals, v_gpu.astype(np.float64)], axis=1).reshape(batch, T, 3 * W)
     else:
         qkv = f("QKV").reshape(batch, T, 3 * W)
     ref_attn = _attn_ref(qkv[..., :W], qkv[..., W:2 * W], qkv[..., 2 * W:], H, D, 1 / math.sqrt(D)).reshape(M, W)
     attn_extra = _attn_extra(qkv[..., 2 * W:], H, D).reshape(M, W) + 1e-6
-    if attn_fp8:
+    if pv8:
         # e4m3 probabilities: each p_t carries a relative rounding error of at
         # most 2^-4 (3 mantissa bits), so the normalized sum moves by at most
         # 2^-4 / (1 - 2^-4) * max_t |v_t - o|; twice that covers the few keys
@@ -321,7 +336,7 @@ def check_stages(model, wt, x, dims, fp8, batch, attn_fp8=False):
         vmax = np.abs(v4).max(axis=1)                                  # [batch, H, D]
         spread = vmax[:, None, :, :] + np.abs(ref_attn.reshape(batch, T, H, D))
         attn_extra = attn_extra + (2 * 2.0 ** -4 / (1 - 2.0 ** -4) * spread).reshape(M, W)
-    if fp8 and attn_fp8:
+    if fp8 and pv8:
         e4m3_within("ATTN", st["ATTN"], ref_attn, se, band=attn_extra)
     elif fp8:
         e4m3_neighbours_ok("ATTN", st["ATTN"], ref_attn, se, band=attn_extra)
@@ -400,22 +415,24 @@ def test_c0_single_layer_stage_by_stage_and_end_to_end(V, fp8, explicit_kv):
         assert cos.min() >= 0.99 and mx.max() <= 0.5
 
 
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["pv", "qk", "qk_pv"])
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16_gemm", "fp8_gemm"])
-def test_c0_attention_fp8_stages_and_end_to_end(V, fp8):
-    """The e4m3 PV option: V^T codes, the attention stage within the bound
-    of e4m3 probabilities, every other stage as before, and the whole model
-    within the tolerance of its GEMM precision."""
+def test_c0_attention_fp8_stages_and_end_to_end(V, fp8, mode):
+    """The e4m3 attention products (PV, QK or both): V^T or Q/K codes, the
+    attention stage against the oracle on the decoded codes (within the bound
+    of e4m3 probabilities when PV is e4m3), every other stage as before, and
+    the whole model within the tolerance of its GEMM precision."""
     cfg = S.CONFIGS["c0_1layer_b1_f16"]
     dims = S.SO400M.with_depth(1)
-    _flush(f"c0 attention_fp8 fp8_gemm={fp8}")
-    model, wt = make_model(V, dims, cfg["seed"], max_batch=2, fp8=fp8, attention_fp8=True)
+    _flush(f"c0 attention_fp8={mode} fp8_gemm={fp8}")
+    model, wt = make_model(V, dims, cfg["seed"], max_batch=2, fp8=fp8, attention_fp8=mode)
     model.debug_capture(0)
     x = S.make_pixels(dims, 2, cfg["seed"])
     y = run(model, x)
-    check_stages(model, wt, x, dims, fp8, 2, attn_fp8=True)
+    check_stages(model, wt, x, dims, fp8, 2, attn_fp8=mode)
     ref = O.encode(wt, x, dims.heads)
     cos, mx = per_image_metrics(y, ref)
-    _flush(f"  c0 attention_fp8 end-to-end fp8_gemm={fp8}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    _flush(f"  c0 attention_fp8={mode} end-to-end fp8_gemm={fp8}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
     if not fp8:
         assert cos.min() >= 0.999 and mx.max() <= 2e-2
     else:
@@ -469,10 +486,11 @@ def test_determinism_and_nan_poisoned_workspace(V):
     b = model8.encode(xt).cpu().numpy()
     np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
     assert np.isfinite(a).all()
-    # e4m3 PV attention: 0x7F7F is a NaN in F16 and, byte by byte, in e4m3, so
-    # the V^T rows past each head's 72 that the kernel reads (and the slack
-    # after the last head) hold NaN codes; they must not reach the output
-    model8p, _ = make_model(V, dims, 0, max_batch=3, fp8=True, attention_fp8=True)
+    # e4m3 QK and PV attention: 0x7F7F is a NaN in F16 and, byte by byte, in
+    # e4m3, so the V^T rows past each head's 72 that the kernel reads (and the
+    # slack after the last head) and bytes 72..79 of every Q/K head slot hold
+    # NaN codes; they must not reach the output
+    model8p, _ = make_model(V, dims, 0, max_batch=3, fp8=True, attention_fp8=3)
     model8p.debug_fill_workspace(0)
     a = model8p.encode(xt).cpu().numpy()
     model8p.debug_fill_workspace(0x7F7F)
@@ -540,14 +558,15 @@ def test_graph_capture_replays_match_eager(V, batch):
     model.close()
 
 
-@pytest.mark.parametrize("fp8,attn_fp8", [(False, False), (True, False), (True, True)],
-                         ids=["f16", "fp8", "fp8_e4m3_pv"])
+@pytest.mark.parametrize("fp8,attn_fp8", [(False, 0), (True, 0), (True, 1), (True, 3), (False, 2)],
+                         ids=["f16", "fp8", "fp8_e4m3_pv", "fp8_e4m3_qk_pv", "f16_e4m3_qk"])
 def test_separate_qkv_matches_fused_bitwise(V, fp8, attn_fp8):
     """Separate Q/K/V (and MAP K/V) projections against the fused ones: every
     output element has the same operands and summation order, so results are
     identical, at batch 2 (small tiles) and batch 64 (the large-batch tile
     shapes, where the fused and separate widths take different tiles); with
-    e4m3 PV attention the separate V projection writes the e4m3 V^T codes."""
+    e4m3 attention products the separate projections write the e4m3 V^T and
+    Q/K codes."""
     dims = S.SO400M.with_depth(2)
     wt = S.make_weights(dims, 3)
     blob = S.pack_blob(dims, wt)
@@ -642,23 +661,25 @@ def test_c4_27_layers_fp8_b64_sampled(V):
     assert cos.min() >= 0.99 and mx.max() <= 0.5
 
 
-def test_c4_attention_fp8_27_layers_b64_sampled(V):
-    """The c4 workload with the e4m3 PV option, against the unquantized
-    oracle on the sampled images (page "FP8 attention and resident
-    image/embedding transfers", "Full 27-layer ViT": every FP8 attention
-    variant clears cosine > 0.99 there)."""
+@pytest.mark.parametrize("mode", [1, 2, 3], ids=["pv", "qk", "qk_pv"])
+def test_c4_attention_fp8_27_layers_b64_sampled(V, mode):
+    """The c4 workload with e4m3 attention products (PV, QK or both), against
+    the unquantized oracle on the sampled images, to the 27-layer bar (page
+    "FP8 attention and resident image/embedding transfers", "Full 27-layer
+    ViT": every FP8 attention variant clears cosine > 0.99 there)."""
     g = _golden("oracle_c4_27layer_seed2.npz")
     dims = S.SO400M
-    _flush("c4 27 layers FP8 GEMMs + e4m3 PV, B=64")
+    _flush(f"c4 27 layers FP8 GEMMs + e4m3 attention products {mode}, B=64")
     wt = S.make_weights(dims, 2)
     x = S.make_pixels(dims, 64, 2)
-    model = V.Model(S.pack_blob(dims, wt), max_batch=64, fp8=True, attention_fp8=True)
+    model = V.Model(S.pack_blob(dims, wt), max_batch=64, fp8=True, attention_fp8=mode)
     del wt
     y = run(model, x)
+    model.close()
     assert np.isfinite(y).all()
     cos, mx = per_image_metrics(y[g["images"]], g["out"][:, None, :])
-    _flush(f"  c4 + e4m3 PV vs unquantized oracle: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
-    assert cos.min() >= 0.99
+    _flush(f"  c4 + e4m3 attention {mode} vs unquantized oracle: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    assert cos.min() >= 0.99 and mx.max() <= 0.5
 
 
 def test_launch_timing_hook_counts_only_selected_classes(V):

@@ -115,11 +115,14 @@ class Model:
 
     def __init__(self, blob, layers: int = 0, max_batch: int = 1, fp8: bool = False,
                  fp8_scale_exp: int = -4, separate_qkv: bool = False, map_explicit_kv: bool = False,
-                 attention_fp8: bool = False):
+                 attention_fp8=0):
+        """attention_fp8: e4m3 attention products, siglip_options bits (1 = PV,
+        2 = QK, 3 = both); True means PV."""
         lib = load_library()
         keep, ptr, n = _host_ptr(blob)
+        afp8 = 1 if attention_fp8 is True else int(attention_fp8)
         opt = siglip_options(layers, max_batch, 1 if fp8 else 0, fp8_scale_exp, 1 if separate_qkv else 0,
-                             1 if map_explicit_kv else 0, 1 if attention_fp8 else 0)
+                             1 if map_explicit_kv else 0, afp8)
         h = ctypes.c_void_p()
         _check(lib.siglip_create(ptr, n, ctypes.byref(opt), ctypes.byref(h)))
         self._h = h

@@ -273,6 +273,34 @@ constexpr int VK_BYTES = KB * VK_PITCH;          // 11 x 1 KiB
 constexpr int VV_PITCH = 128;
 constexpr int VT_STAGE = VK_BYTES + VROWS * VV_PITCH;
 constexpr int VT_STAGES_DEFAULT = 2;  // 48 KiB per workgroup: three workgroups per CU
+// e4m3 Q and K (QK8): a key's codes sit in a head slot of kQK8Pitch bytes (dims
+// 0..D-1, the rest not read into an MFMA operand); the K stage holds 64 such
+// rows, and each 32-key score tile takes two 32x32x64 e4m3 MFMAs (dims 0..63,
+// then dims 64..D-1 with zero-filled operand bytes above D).
+constexpr int kQK8Pitch = 80;
+constexpr int VK8_BYTES = KB * kQK8Pitch;        // 5 x 1 KiB
+
+// i32x8 fragment of 32 e4m3 codes at p (two 16-byte reads)
+__device__ __forceinline__ i32x8 load32b(const uint8_t* p) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(p);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(p + 16);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// second K-step fragment of a D-dim row (dims 64..95 for lane group 0, zero
+// for lane group 1): only the D - 64 real code bytes at p + 64 are read
+template <int D>
+__device__ __forceinline__ i32x8 load_tail8(const uint8_t* p, int fg) {
+  static_assert(D == 64 || D == 72 || D == 80, "head width");
+  i32x8 f = {0, 0, 0, 0, 0, 0, 0, 0};
+  if constexpr (D == 72) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + 64);
+    if (fg == 0) { f[0] = (int)w.x; f[1] = (int)w.y; }
+  } else if constexpr (D == 80) {
+    const i32x4 w = *reinterpret_cast<const i32x4*>(p + 64);
+    if (fg == 0) { f[0] = w[0]; f[1] = w[1]; f[2] = w[2]; f[3] = w[3]; }
+  }
+  return f;
+}
 
 // key held by K tile row i (see the permutation above)
 __device__ __forceinline__ int key_of_row(int i) {
@@ -287,21 +315,29 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1>
+// QK8: q and k are e4m3 codes (head h of a token row at byte h * kQK8Pitch,
+// ld in bytes), their products scaled into c by the caller.
+template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1, bool QK8 = false>
 __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
-    const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
+    const void* __restrict__ qv, const void* __restrict__ kv, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
+  static_assert(!QK8 || QT == 1, "e4m3 Q/K with one query tile per wave");
   constexpr int QWG = 4 * 32 * QT;               // queries per workgroup
   constexpr int NDC = D / 8;                     // 16-byte dim chunks per key
-  constexpr int NK = VK_BYTES / 1024;            // 1 KiB transfers for K per stage
+  constexpr int KBYTES = QK8 ? VK8_BYTES : VK_BYTES;
+  constexpr int STAGE = KBYTES + VROWS * VV_PITCH;
+  constexpr int NK = KBYTES / 1024;              // 1 KiB transfers for K per stage
   constexpr int NDMA = NK + D / 8;               // 1 KiB transfers per stage
   constexpr int PER_WAVE = (NDMA + 3) / 4;       // every wave issues the same count
   constexpr int RL = (D - 64) / 2;               // oacc[.][2] register holding O^T row D (lane group 0)
   constexpr float kTau = 8.0f;                   // rescale only when a row max grows by > 2^8
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[VT_STAGES * VT_STAGE + 1024];
-  uint8_t* trash = smem + VT_STAGES * VT_STAGE;  // target of the padding transfers
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[VT_STAGES * STAGE + 1024];
+  uint8_t* trash = smem + VT_STAGES * STAGE;     // target of the padding transfers
+  const f16* q = static_cast<const f16*>(qv);
+  const f16* k = static_cast<const f16*>(kv);
+  const uint8_t* kb8 = static_cast<const uint8_t*>(kv);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -321,16 +357,26 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   const f16* vth = vt + (int64_t)bh * D * vt_ld;  // this head's V^T rows
 
   f16x8 qf[QT][5];
-#pragma unroll
-  for (int u = 0; u < QT; ++u)
-#pragma unroll
-    for (int s = 0; s < 5; ++s) {
-      const int d0 = 16 * s + 8 * fg;
-      if (qi[u] < T && d0 < D)
-        qf[u][s] = *reinterpret_cast<const f16x8*>(q + (img + qi[u]) * ld + hc + d0);
-      else
-        qf[u][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  i32x8 q8[2];
+  if constexpr (QK8) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(qv) + (img + qi[0]) * ld + h * kQK8Pitch;
+    q8[0] = q8[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (qi[0] < T) {
+      q8[0] = load32b(qrow + 32 * fg);
+      q8[1] = load_tail8<D>(qrow, fg);
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < QT; ++u)
+#pragma unroll
+      for (int s = 0; s < 5; ++s) {
+        const int d0 = 16 * s + 8 * fg;
+        if (qi[u] < T && d0 < D)
+          qf[u][s] = *reinterpret_cast<const f16x8*>(q + (img + qi[u]) * ld + hc + d0);
+        else
+          qf[u][s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+  }
   // The Q fragments must be complete before the block loop: an explicit,
   // compiler-visible wait here keeps the compiler from inserting a full
   // vmcnt(0) before the first MFMA of every block, which would also drain
@@ -341,7 +387,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
   for (int i = t; i < VT_STAGES * ZCH; i += 256) {
     const int r = i % ZCH;
-    uint8_t* z = smem + (i / ZCH) * VT_STAGE + VK_BYTES + D * VV_PITCH + r * 16;
+    uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
     const int one = 0x3C003C00;  // two F16 ones
     *reinterpret_cast<i32x4*>(z) = r < VV_PITCH / 16 ? i32x4{one, one, one, one} : i32x4{0, 0, 0, 0};
   }
@@ -358,10 +404,18 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   for (int j = 0; j < PER_WAVE; ++j) {
     const int jg = wave + 4 * j;
     const int off = jg * 1024 + 16 * lane;
-    kkey[j] = key_of_row(off / VK_PITCH);
-    kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
+    if constexpr (QK8) {  // K row of kQK8Pitch code bytes: 5 chunks of 16
+      kkey[j] = key_of_row(off / kQK8Pitch);
+      kdc[j] = (off % kQK8Pitch) / 16;
+    } else {
+      kkey[j] = key_of_row(off / VK_PITCH);
+      kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
+    }
     if (jg < NK) {
-      src[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
+      if constexpr (QK8)
+        src[j] = reinterpret_cast<const f16*>(kb8 + (img + kkey[j]) * ld + h * kQK8Pitch + 16 * kdc[j]);
+      else
+        src[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
     } else if (jg < NDMA) {
       const int d = 8 * (jg - NK) + vd_lo;
       src[j] = vth + (int64_t)d * vt_ld + 8 * (vchunk ^ vswz_key(d));
@@ -371,17 +425,22 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   }
   auto issue = [&](int kb) {
     const int key0 = kb * KB;
-    uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
+    uint8_t* st = smem + (kb % VT_STAGES) * STAGE;
     const bool tail = key0 + KB > T;  // keys past T re-read token T-1
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int jg = wave + 4 * j;
       if (jg < NK) {
-        const f16* p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
-                            : src[j] + (int64_t)key0 * ld;
+        const void* p;
+        if constexpr (QK8)
+          p = tail ? kb8 + (img + min(key0 + kkey[j], T - 1)) * ld + h * kQK8Pitch + 16 * kdc[j]
+                   : reinterpret_cast<const uint8_t*>(src[j]) + (int64_t)key0 * ld;
+        else
+          p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
+                   : src[j] + (int64_t)key0 * ld;
         dma16(p, st + jg * 1024);
       } else if (jg < NDMA) {
-        dma16(src[j] + key0, st + VK_BYTES + (jg - NK) * 1024);
+        dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
       } else {
         dma16(src[j], trash);
       }
@@ -392,7 +451,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   const int koff = fr * VK_PITCH + fg * 16;                      // + kt*32*176 + s*32
   int voff[4];                                                   // + dt*32*128
 #pragma unroll
-  for (int s = 0; s < 4; ++s) voff[s] = VK_BYTES + fr * VV_PITCH + 16 * ((2 * s + fg) ^ vswz_key(fr));
+  for (int s = 0; s < 4; ++s) voff[s] = KBYTES + fr * VV_PITCH + 16 * ((2 * s + fg) ^ vswz_key(fr));
 
   float m_run[QT];
   f32x16 oacc[QT][3];
@@ -416,7 +475,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
       attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (kb + VT_STAGES - 1 < nkb) issue(kb + VT_STAGES - 1);  // into the stage block kb-1 used
-    const uint8_t* st = smem + (kb % VT_STAGES) * VT_STAGE;
+    const uint8_t* st = smem + (kb % VT_STAGES) * STAGE;
     const int key0 = kb * KB;
 
     // S^T for every query tile; each K fragment read feeds QT MFMAs
@@ -427,12 +486,21 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
       for (int u = 0; u < QT; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[u][kt][r] = 0.0f;
+      if constexpr (QK8) {
+        const uint8_t* kr = st + (kt * 32 + fr) * kQK8Pitch;
+        sacc[0][kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(load32b(kr + 32 * fg), q8[0], sacc[0][kt],
+                                                                      0, 0, 0, 127, 0, 127);
+        if constexpr (D > 64)
+          sacc[0][kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(load_tail8<D>(kr, fg), q8[1], sacc[0][kt],
+                                                                        0, 0, 0, 127, 0, 127);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 5; ++s) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
+        for (int s = 0; s < 5; ++s) {
+          const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
 #pragma unroll
-        for (int u = 0; u < QT; ++u)
-          sacc[u][kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[u][s], sacc[u][kt], 0, 0, 0);
+          for (int u = 0; u < QT; ++u)
+            sacc[u][kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[u][s], sacc[u][kt], 0, 0, 0);
+        }
       }
     }
     if (key0 + KB > T) {
@@ -558,23 +626,28 @@ __device__ __forceinline__ int key_of_row8(int row) {
 }
 __device__ __forceinline__ int vswz8(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
-template <int D, bool OUT_FP8>
+template <int D, bool OUT_FP8, bool QK8 = false>
 __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
-    const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const uint8_t* __restrict__ vt,
+    const void* __restrict__ qv, const void* __restrict__ kv, int64_t ld, const uint8_t* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale,
     float v_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
   constexpr int STAGES = 2;
   constexpr int QWG = 4 * 32;                    // queries per workgroup
   constexpr int NDC = D / 8;                     // 16-byte dim chunks per key (F16 K)
-  constexpr int NK = VK_BYTES / 1024;            // 1 KiB transfers for K per stage
+  constexpr int KBYTES = QK8 ? VK8_BYTES : VK_BYTES;
+  constexpr int STAGE = KBYTES + VROWS * VV8_PITCH;
+  constexpr int NK = KBYTES / 1024;              // 1 KiB transfers for K per stage
   constexpr int NV = VV8_ROWS_DMA * VV8_PITCH / 1024;  // 1 KiB transfers for V^T per stage
   constexpr int NDMA = NK + NV;
   constexpr int PER_WAVE = (NDMA + 3) / 4;
   constexpr int RL = 8;                          // oacc[2] register holding O^T row 80 (lane group 0)
   constexpr float kTau = 4.0f;                   // probabilities stay <= 2^4
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * VT8_STAGE + 1024];
-  uint8_t* trash = smem + STAGES * VT8_STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 1024];
+  uint8_t* trash = smem + STAGES * STAGE;
+  const f16* q = static_cast<const f16*>(qv);
+  const f16* k = static_cast<const f16*>(kv);
+  const uint8_t* kb8 = static_cast<const uint8_t*>(kv);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -592,13 +665,23 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
   const uint8_t* vth = vt + (int64_t)bh * D * vt_ld;
 
   f16x8 qf[5];
+  i32x8 q8[2];
+  if constexpr (QK8) {
+    const uint8_t* qrow = static_cast<const uint8_t*>(qv) + (img + qi) * ld + h * kQK8Pitch;
+    q8[0] = q8[1] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (qi < T) {
+      q8[0] = load32b(qrow + 32 * fg);
+      q8[1] = load_tail8<D>(qrow, fg);
+    }
+  } else {
 #pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    const int d0 = 16 * s + 8 * fg;
-    if (qi < T && d0 < D)
-      qf[s] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
-    else
-      qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    for (int s = 0; s < 5; ++s) {
+      const int d0 = 16 * s + 8 * fg;
+      if (qi < T && d0 < D)
+        qf[s] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
+      else
+        qf[s] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   // constant V^T rows 80..95 of every stage: row 80 = e4m3(2^-exp), the rest 0
@@ -608,7 +691,7 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
     constexpr int ZCH = (VROWS - VV8_ROWS_DMA) * VV8_PITCH / 16;
     for (int i = t; i < STAGES * ZCH; i += 256) {
       const int r = i % ZCH;
-      uint8_t* z = smem + (i / ZCH) * VT8_STAGE + VK_BYTES + VV8_ROWS_DMA * VV8_PITCH + r * 16;
+      uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + VV8_ROWS_DMA * VV8_PITCH + r * 16;
       *reinterpret_cast<i32x4*>(z) =
           r < VV8_PITCH / 16 ? i32x4{(int)one4, (int)one4, (int)one4, (int)one4} : i32x4{0, 0, 0, 0};
     }
@@ -618,21 +701,30 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
   // transfer slots (slot j of this wave: global index jg = wave + 4 j); a
   // V^T transfer fills 16 rows of 64 bytes, lane i row i / 4, physical
   // chunk i % 4
-  const f16* ksrc[PER_WAVE];
+  const uint8_t* ksrc[PER_WAVE];  // byte addresses (F16 or e4m3 K)
   const uint8_t* vsrc[PER_WAVE];
   int kkey[PER_WAVE], kdc[PER_WAVE];
+  // byte offset of a key's row start and of a 16-byte chunk of it
+  const int64_t krow = QK8 ? ld : 2 * ld;
+  const int64_t kcol = QK8 ? (int64_t)h * kQK8Pitch : 2 * (int64_t)hc;
+  constexpr int KCH_BYTES = 16;
 #pragma unroll
   for (int j = 0; j < PER_WAVE; ++j) {
     const int jg = wave + 4 * j;
     kkey[j] = 0;
     kdc[j] = 0;
-    ksrc[j] = k + img * ld + hc;
+    ksrc[j] = kb8 + img * krow + kcol;
     vsrc[j] = vth;
     if (jg < NK) {
       const int off = jg * 1024 + 16 * lane;
-      kkey[j] = key_of_row8(off / VK_PITCH);
-      kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
-      ksrc[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
+      if constexpr (QK8) {
+        kkey[j] = key_of_row8(off / kQK8Pitch);
+        kdc[j] = (off % kQK8Pitch) / 16;
+      } else {
+        kkey[j] = key_of_row8(off / VK_PITCH);
+        kdc[j] = min((off % VK_PITCH) / 16, NDC - 1);
+      }
+      ksrc[j] = kb8 + (img + kkey[j]) * krow + kcol + KCH_BYTES * kdc[j];
     } else if (jg < NDMA) {
       const int vr = 16 * (jg - NK) + (lane >> 2);
       vsrc[j] = vth + (int64_t)vr * vt_ld + 16 * vswz8(vr, lane & 3);
@@ -640,17 +732,17 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
   }
   auto issue = [&](int kb) {
     const int key0 = kb * KB;
-    uint8_t* st = smem + (kb % STAGES) * VT8_STAGE;
+    uint8_t* st = smem + (kb % STAGES) * STAGE;
     const bool tail = key0 + KB > T;  // keys past T re-read token T-1
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int jg = wave + 4 * j;
       if (jg < NK) {
-        const f16* p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
-                            : ksrc[j] + (int64_t)key0 * ld;
+        const uint8_t* p = tail ? kb8 + (img + min(key0 + kkey[j], T - 1)) * krow + kcol + KCH_BYTES * kdc[j]
+                                : ksrc[j] + (int64_t)key0 * krow;
         dma16(p, st + jg * 1024);
       } else if (jg < NDMA) {
-        dma16(vsrc[j] + key0, st + VK_BYTES + (jg - NK) * 1024);
+        dma16(vsrc[j] + key0, st + KBYTES + (jg - NK) * 1024);
       } else {
         dma16(ksrc[0], trash);
       }
@@ -665,7 +757,7 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int row = 32 * dt + fr;
-      voff[dt][h2] = VK_BYTES + row * VV8_PITCH + 16 * vswz8(row, 2 * fg + h2);
+      voff[dt][h2] = KBYTES + row * VV8_PITCH + 16 * vswz8(row, 2 * fg + h2);
     }
 
   float m_run = kNegInf;
@@ -681,7 +773,7 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
     attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (kb + 1 < nkb) issue(kb + 1);  // into the stage block kb-1 used
-    const uint8_t* st = smem + (kb % STAGES) * VT8_STAGE;
+    const uint8_t* st = smem + (kb % STAGES) * STAGE;
     const int key0 = kb * KB;
 
     f32x16 sacc[2];
@@ -689,10 +781,19 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.0f;
+      if constexpr (QK8) {
+        const uint8_t* kr = st + (kt * 32 + fr) * kQK8Pitch;
+        sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(load32b(kr + 32 * fg), q8[0], sacc[kt], 0, 0, 0,
+                                                                   127, 0, 127);
+        if constexpr (D > 64)
+          sacc[kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(load_tail8<D>(kr, fg), q8[1], sacc[kt], 0, 0, 0,
+                                                                     127, 0, 127);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 5; ++s) {
-        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
+        for (int s = 0; s < 5; ++s) {
+          const f16x8 kf = *reinterpret_cast<const f16x8*>(st + koff + kt * 32 * VK_PITCH + s * 32);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[s], sacc[kt], 0, 0, 0);
+        }
       }
     }
     if (key0 + KB > T) {
@@ -763,18 +864,18 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
     }
 }
 
-template <int D>
-hipError_t launch_vt_d(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o, int64_t ldo,
+template <int D, bool QK8>
+hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o, int64_t ldo,
                        int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale, hipStream_t s) {
   const int nqb = (tokens + QB - 1) / QB;
   const int64_t blocks = (int64_t)nqb * heads * batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (out_fp8)
-    hipLaunchKernelGGL((flash_attn_vt_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt, vt_ld,
-                       o, ldo, tokens, heads, nqb, sl2, out_scale);
+    hipLaunchKernelGGL((flash_attn_vt_kernel<D, true, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
   else
-    hipLaunchKernelGGL((flash_attn_vt_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt,
-                       vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
+    hipLaunchKernelGGL((flash_attn_vt_kernel<D, false, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
   return hipGetLastError();
 }
 
@@ -886,53 +987,73 @@ hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v, int6
 
 bool flash_attention_vt_supported(int head_dim) { return head_dim == 64 || head_dim == 72 || head_dim == 80; }
 
-hipError_t launch_flash_attention_vt(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o,
-                                     int64_t ldo, int batch, int heads, int tokens, int head_dim, float scale,
-                                     bool out_fp8, float out_scale, hipStream_t s) {
+namespace {
+// Q/K operand checks shared by the V^T launchers: F16 rows of ld elements, or
+// e4m3 code rows of ld bytes with head slots of kQK8Pitch bytes (16-byte
+// aligned rows and slots, every slot of a row inside ld).
+bool qk_args_ok(const void* q, const void* k, int64_t ld, int heads, int head_dim, int qk8_pitch) {
+  if (qk8_pitch == 0) return ld >= (int64_t)heads * head_dim && (ld & 7) == 0;
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  return qk8_pitch == kQK8Pitch && head_dim <= kQK8Pitch && ld >= (int64_t)heads * kQK8Pitch && (ld & 15) == 0 &&
+         a16(q) && a16(k);
+}
+}  // namespace
+
+hipError_t launch_flash_attention_vt(const void* q, const void* k, int64_t ld, int qk8_pitch, const f16* vt,
+                                     int64_t vt_ld, void* o, int64_t ldo, int batch, int heads, int tokens,
+                                     int head_dim, float scale, bool out_fp8, float out_scale, hipStream_t s) {
   if (batch < 1 || heads < 1 || tokens < 1 || !flash_attention_vt_supported(head_dim) ||
-      ld < (int64_t)heads * head_dim || (ld & 7) || ldo < (int64_t)heads * head_dim || (ldo & 3) ||
+      !qk_args_ok(q, k, ld, heads, head_dim, qk8_pitch) || ldo < (int64_t)heads * head_dim || (ldo & 3) ||
       vt_ld < (int64_t)(tokens + KB - 1) / KB * KB || (vt_ld & 7))
     return hipErrorInvalidValue;
-  const float sl2 = scale * 1.4426950408889634f;
-  switch (head_dim) {
-    case 64: return launch_vt_d<64>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
-    case 72: return launch_vt_d<72>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
-    case 80: return launch_vt_d<80>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+  // e4m3 Q and K codes carry 2^4 each: their products are 2^8 times the scores
+  const float sl2 = scale * 1.4426950408889634f * (qk8_pitch ? 1.0f / 256.0f : 1.0f);
+  switch (head_dim * 2 + (qk8_pitch ? 1 : 0)) {
+    case 128: return launch_vt_d<64, false>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 144: return launch_vt_d<72, false>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 160: return launch_vt_d<80, false>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 129: return launch_vt_d<64, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 145: return launch_vt_d<72, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 161: return launch_vt_d<80, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
   }
   return hipErrorInvalidValue;
 }
 
 namespace {
-template <int D>
-hipError_t launch_vt8_d(const f16* q, const f16* k, int64_t ld, const uint8_t* vt, int64_t vt_ld, void* o,
+template <int D, bool QK8>
+hipError_t launch_vt8_d(const void* q, const void* k, int64_t ld, const uint8_t* vt, int64_t vt_ld, void* o,
                         int64_t ldo, int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale,
                         float v_scale, hipStream_t s) {
   const int nqb = (tokens + QB - 1) / QB;
   const int64_t blocks = (int64_t)nqb * heads * batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (out_fp8)
-    hipLaunchKernelGGL((flash_attn_vt8_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt, vt_ld,
-                       o, ldo, tokens, heads, nqb, sl2, out_scale, v_scale);
+    hipLaunchKernelGGL((flash_attn_vt8_kernel<D, true, QK8>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt,
+                       vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale, v_scale);
   else
-    hipLaunchKernelGGL((flash_attn_vt8_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt,
+    hipLaunchKernelGGL((flash_attn_vt8_kernel<D, false, QK8>), dim3((unsigned)blocks), dim3(256), 0, s, q, k, ld, vt,
                        vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale, v_scale);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_flash_attention_vt8(const f16* q, const f16* k, int64_t ld, const uint8_t* vt, int64_t vt_ld,
-                                      void* o, int64_t ldo, int batch, int heads, int tokens, int head_dim,
-                                      float scale, bool out_fp8, float out_scale, float v_scale, hipStream_t s) {
+hipError_t launch_flash_attention_vt8(const void* q, const void* k, int64_t ld, int qk8_pitch, const uint8_t* vt,
+                                      int64_t vt_ld, void* o, int64_t ldo, int batch, int heads, int tokens,
+                                      int head_dim, float scale, bool out_fp8, float out_scale, float v_scale,
+                                      hipStream_t s) {
   if (batch < 1 || heads < 1 || tokens < 1 || !flash_attention_vt_supported(head_dim) ||
-      ld < (int64_t)heads * head_dim || (ld & 7) || ldo < (int64_t)heads * head_dim || (ldo & 3) ||
+      !qk_args_ok(q, k, ld, heads, head_dim, qk8_pitch) || ldo < (int64_t)heads * head_dim || (ldo & 3) ||
       vt_ld < (int64_t)(tokens + KB - 1) / KB * KB || (vt_ld & 15) ||
       (reinterpret_cast<uintptr_t>(vt) & 15) || !(v_scale > 0.0f) || v_scale > 256.0f)
     return hipErrorInvalidValue;
-  const float sl2 = scale * 1.4426950408889634f;
-  switch (head_dim) {
-    case 64: return launch_vt8_d<64>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
-    case 72: return launch_vt8_d<72>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
-    case 80: return launch_vt8_d<80>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+  const float sl2 = scale * 1.4426950408889634f * (qk8_pitch ? 1.0f / 256.0f : 1.0f);
+  switch (head_dim * 2 + (qk8_pitch ? 1 : 0)) {
+    case 128: return launch_vt8_d<64, false>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 144: return launch_vt8_d<72, false>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 160: return launch_vt8_d<80, false>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 129: return launch_vt8_d<64, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 145: return launch_vt8_d<72, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
+    case 161: return launch_vt8_d<80, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
   }
   return hipErrorInvalidValue;
 }

@@ -91,9 +91,11 @@ enum GemmEpi : int {
   EPI_BIAS_POS = 1,  // acc*s + bias[n] + pos[m % pos_rows][n]
   EPI_BIAS_RES = 2,  // acc*s + bias[n] + res[m][n]
   EPI_BIAS_GELU = 3, // gelu(acc*s + bias[n])
-  EPI_QKV = 4        // acc*s + bias[n]; columns >= vt_col0 (the V part) go to
+  EPI_QKV = 4,       // acc*s + bias[n]; columns >= vt_col0 (the V part) go to
                      // vt transposed per head instead of to c (as F16, or as
                      // e4m3 codes of value*out_scale when out_fp8 is set)
+  EPI_QKV8 = 5       // as EPI_QKV, with the columns < vt_col0 (Q and K) written
+                     // as e4m3 codes into the head slots of qk8 instead of to c
 };
 
 struct GemmArgs {
@@ -112,6 +114,10 @@ struct GemmArgs {
   f16* vt; int vt_col0, vt_tokens, vt_heads, vt_dim; int64_t vt_ld;
   float vt_inv_dim;  // 1 / vt_dim
   int group_m;       // tile-order band height in row blocks (<= 0: N-fastest)
+  // EPI_QKV8: column n < vt_col0 (head slot n / vt_dim: Q heads, then K
+  // heads) is written as the e4m3 code of value*qk8_scale at byte
+  // qk8 + m*qk8_ld + (n / vt_dim)*qk8_pitch + n % vt_dim
+  uint8_t* qk8; int64_t qk8_ld; int qk8_pitch; float qk8_scale;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8,
@@ -132,21 +138,25 @@ hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v,
 
 // Encoder attention with V given transposed per head: vt row (b*heads + h)*
 // head_dim + d holds keys 0..tokens-1 of that (image, head, dim), row stride
-// vt_ld >= round_up(tokens, 64), zeros in columns tokens..vt_ld-1. q and k as
-// for launch_flash_attention. head_dim must be 64, 72 or 80.
-hipError_t launch_flash_attention_vt(const f16* q, const f16* k, int64_t ld, const f16* vt, int64_t vt_ld,
-                                     void* o, int64_t ldo, int batch, int heads, int tokens,
-                                     int head_dim, float scale, bool out_fp8, float out_scale,
-                                     hipStream_t s);
+// vt_ld >= round_up(tokens, 64), zeros in columns tokens..vt_ld-1. head_dim
+// must be 64, 72 or 80. With qk8_pitch = 0, q and k are F16 as for
+// launch_flash_attention (ld in elements). With qk8_pitch = 80, they are
+// e4m3 codes of 2^4 times the values: token row t at q + t*ld bytes, head h
+// at byte h*80 (bytes head_dim..79 of a slot are never used in a product),
+// ld a multiple of 16, q and k 16-byte aligned.
+hipError_t launch_flash_attention_vt(const void* q, const void* k, int64_t ld, int qk8_pitch, const f16* vt,
+                                     int64_t vt_ld, void* o, int64_t ldo, int batch, int heads, int tokens,
+                                     int head_dim, float scale, bool out_fp8, float out_scale, hipStream_t s);
 
 // The same with the PV product in e4m3: vt holds codes of v * v_scale (bytes,
 // row stride vt_ld, a multiple of 16, zero codes in columns tokens..vt_ld-1;
 // the 80 - head_dim rows after the last head's must be readable), the
 // probabilities are quantized to e4m3(p * 2^4) in registers. v_scale is a
 // power of two in (0, 256].
-hipError_t launch_flash_attention_vt8(const f16* q, const f16* k, int64_t ld, const uint8_t* vt, int64_t vt_ld,
-                                      void* o, int64_t ldo, int batch, int heads, int tokens, int head_dim,
-                                      float scale, bool out_fp8, float out_scale, float v_scale, hipStream_t s);
+hipError_t launch_flash_attention_vt8(const void* q, const void* k, int64_t ld, int qk8_pitch, const uint8_t* vt,
+                                      int64_t vt_ld, void* o, int64_t ldo, int batch, int heads, int tokens,
+                                      int head_dim, float scale, bool out_fp8, float out_scale, float v_scale,
+                                      hipStream_t s);
 bool flash_attention_vt_supported(int head_dim);
 
 hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv,

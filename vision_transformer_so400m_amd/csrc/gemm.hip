@@ -63,7 +63,7 @@ template <int EPI, bool OUT_FP8>
 struct StageType {
   typedef typename std::conditional<
       EPI == EPI_BIAS_RES, float,
-      typename std::conditional<OUT_FP8 && EPI != EPI_QKV, uint8_t, f16>::type>::type type;
+      typename std::conditional<(OUT_FP8 && EPI != EPI_QKV) || EPI == EPI_QKV8, uint8_t, f16>::type>::type type;
 };
 
 // Linear workgroup id -> output tile. Workgroups are dispatched round-robin
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
   }
 
   // ---- epilogue: lane holds row m = tile row + fr, columns 8q + 4fg + (0..3)
-  if constexpr (EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_QKV || EPI == EPI_QKV8) {
     if (n0 + wn * WN >= g.vt_col0) {
       // V columns (whole waves: vt_col0 is a multiple of 128): 4 consecutive
       // dims of one head written transposed. The 32 lanes of a half-wave hold
@@ -318,13 +318,32 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
         } else if constexpr (SB == 2) {
           *reinterpret_cast<f16x4*>(saddr(r, 2 * c)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
         } else {
-          *reinterpret_cast<uint32_t*>(saddr(r, c)) =
-              pack4_e4m3(v[0] * g.out_scale, v[1] * g.out_scale, v[2] * g.out_scale, v[3] * g.out_scale);
+          const float sc = EPI == EPI_QKV8 ? g.qk8_scale : g.out_scale;
+          *reinterpret_cast<uint32_t*>(saddr(r, c)) = pack4_e4m3(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
         }
       }
     }
   }
   __syncthreads();
+  if constexpr (EPI == EPI_QKV8) {
+    // e4m3 Q/K codes into head slots: 8 consecutive columns never cross a
+    // head (vt_dim % 8 == 0, n0 % 8 == 0), so each 8-byte group of a staged
+    // row is one 8-byte store; consecutive threads take consecutive groups
+    constexpr int G = BN / 8;
+#pragma unroll 4
+    for (int u = t; u < BM * G; u += T::THREADS) {
+      const int r = u / G;
+      const int c = (u - r * G) * 8;
+      const int m = m0 + r;
+      if (m >= g.M) continue;
+      const int n = n0 + c;
+      const int hh = (int)(((float)n + 0.5f) * g.vt_inv_dim);  // exact: n < 2^20, dim <= 2^10
+      const int dd = n - hh * g.vt_dim;
+      *reinterpret_cast<uint2*>(g.qk8 + (int64_t)m * g.qk8_ld + hh * g.qk8_pitch + dd) =
+          *reinterpret_cast<const uint2*>(saddr(r, c));
+    }
+    return;
+  }
   constexpr int OB = SB == 1 ? 1 : 2;
   constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
   constexpr int VPC = 16 / OB;       // values per output chunk
@@ -377,7 +396,7 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     // 256x256 tiles: not for the residual epilogue (its F32 staged tile
     // would not fit the LDS ring) nor the V-transposing one (a tile must not
     // straddle the V column boundary)
-    if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV)
+    if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV && EPI != EPI_QKV8)
       if (g.N % 256 == 0) {
         if (b.group_m == 0) b.group_m = 4;
         return launch_cfg<256, 256, 128, 64, 2, FP8, EPI, OUT_FP8>(b, s);
@@ -403,6 +422,8 @@ hipError_t launch_epi(const GemmArgs& g, int epi, bool out_fp8, hipStream_t s) {
     case EPI_BIAS_RES: return launch_sized<FP8, EPI_BIAS_RES, false>(g, s);
     case EPI_QKV:
       return out_fp8 ? launch_sized<FP8, EPI_QKV, true>(g, s) : launch_sized<FP8, EPI_QKV, false>(g, s);
+    case EPI_QKV8:
+      return out_fp8 ? launch_sized<FP8, EPI_QKV8, true>(g, s) : launch_sized<FP8, EPI_QKV8, false>(g, s);
     case EPI_BIAS_GELU:
       return out_fp8 ? launch_sized<FP8, EPI_BIAS_GELU, true>(g, s)
                      : launch_sized<FP8, EPI_BIAS_GELU, false>(g, s);
@@ -421,18 +442,23 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   if ((int64_t)g.M * g.lda * E >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   // e4m3 output: the GELU epilogue's output, or V^T of the QKV epilogue
-  if (out_fp8 && epi != EPI_BIAS_GELU && epi != EPI_QKV) return hipErrorInvalidValue;
+  const bool qkv = epi == EPI_QKV || epi == EPI_QKV8;
+  if (out_fp8 && epi != EPI_BIAS_GELU && !qkv) return hipErrorInvalidValue;
   // 16-byte transfers: operand rows, output rows and residual rows aligned
-  const int OB = (out_fp8 && epi != EPI_QKV) ? 1 : 2;
+  const int OB = (out_fp8 && !qkv) ? 1 : 2;
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
   if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * E) % 16 || (g.ldw * E) % 16 ||
       (g.ldc * OB) % 16)
     return hipErrorInvalidValue;
   if (epi == EPI_BIAS_RES && (!g.res || misaligned(g.res) || g.ldres % 8 || g.ldres < g.N))
     return hipErrorInvalidValue;
-  if (epi == EPI_QKV && (!g.vt || g.vt_dim < 4 || g.vt_dim % 4 || g.vt_dim > 1024 || g.vt_col0 % 128 ||
-                         g.vt_tokens < 1 || g.vt_ld < g.vt_tokens || g.N >= (1 << 20) ||
-                         (g.N - g.vt_col0) != g.vt_heads * g.vt_dim))
+  if (qkv && (!g.vt || g.vt_dim < 4 || g.vt_dim % 4 || g.vt_dim > 1024 || g.vt_col0 % 128 ||
+              g.vt_tokens < 1 || g.vt_ld < g.vt_tokens || g.N >= (1 << 20) ||
+              (g.N - g.vt_col0) != g.vt_heads * g.vt_dim))
+    return hipErrorInvalidValue;
+  if (epi == EPI_QKV8 && (!g.qk8 || g.vt_dim % 8 || g.vt_col0 % g.vt_dim || g.qk8_pitch < g.vt_dim ||
+                          g.qk8_pitch % 16 || g.qk8_ld < (int64_t)(g.vt_col0 / g.vt_dim) * g.qk8_pitch ||
+                          g.qk8_ld % 16 || misaligned(g.qk8)))
     return hipErrorInvalidValue;
   return in_fp8 ? launch_epi<true>(g, epi, out_fp8, s) : launch_epi<false>(g, epi, out_fp8, s);
 }

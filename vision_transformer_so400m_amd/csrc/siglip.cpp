@@ -59,6 +59,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int kKAlign = 128;  // K padding (elements): whole 128-byte slices for both F16 and e4m3
 constexpr int kNAlign = 128;  // N padding: the widest GEMM column tile
+constexpr int kQK8SlotBytes = 80;  // e4m3 Q/K head slot: 16-byte aligned rows for the attention's transfers
 
 struct Gemm {
   void* w = nullptr;      // [n_pad, k_pad] F16 or e4m3, K-contiguous
@@ -118,6 +119,8 @@ struct siglip_model {
   int patch_pad = 0, mlp_pad = 0;
   bool vt_path = false;  // V written transposed by the QKV GEMM for the streaming attention
   bool attn_fp8 = false; // PV product in e4m3: V^T as e4m3 codes of v * attn_v_scale
+  bool attn_qk8 = false; // QK product in e4m3: Q and K as e4m3 codes of x * attn_v_scale in the
+                         // QKV buffer's bytes, head h of a token row at byte h * 80 (K after Q)
   float attn_v_scale = 1.0f;
   int tokens_pad = 0;    // V^T row length: tokens rounded up to the 64-key block
 
@@ -346,53 +349,18 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
   hip_check(launch_gemm(args, epi, m->fp8, out_fp8, s), "gemm launch");
 }
 
-// The fused QKV projection: Q and K row-major into qkv, V transposed per
-// head into vt when the streaming attention is used.
-void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* vt, int M, hipStream_t s) {
-  const Gemm& g = Ly.qkv;
-  if (m->separate_qkv) {
-    // Q and K into their columns of the fused row; V as its own projection,
-    // transposed per head (all its columns are V: vt_col0 = 0)
-    const int W = m->width;
-    gemm(m, Ly.q, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
-    gemm(m, Ly.k, a, W, M, qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
-    if (!m->vt_path) {
-      gemm(m, Ly.v, a, W, M, qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
-      return;
-    }
-    GemmArgs args{};
-    args.a = a;
-    args.lda = W;
-    args.w = Ly.v.w;
-    args.ldw = Ly.v.k_pad;
-    args.c = qkv + 2 * W;  // not written: every column goes to vt
-    args.ldc = 3 * W;
-    args.bias = Ly.v.bias;
-    args.M = M;
-    args.N = Ly.v.n_pad;
-    args.K = Ly.v.k_pad;
-    args.acc_scale = m->acc_scale;
-    args.out_scale = m->attn_fp8 ? m->attn_v_scale : m->op_scale;
-    args.vt = static_cast<f16*>(vt);
-    args.vt_col0 = 0;
-    args.vt_tokens = m->tokens;
-    args.vt_heads = m->heads;
-    args.vt_dim = m->head_dim;
-    args.vt_ld = m->tokens_pad;
-    args.vt_inv_dim = 1.0f / (float)m->head_dim;
-    hip_check(launch_gemm(args, EPI_QKV, m->fp8, m->attn_fp8, s), "v gemm launch");
-    return;
-  }
-  if (!m->vt_path) {
-    gemm(m, g, a, m->width, M, qkv, 3 * m->width, EPI_BIAS, false, nullptr, 0, s);
-    return;
-  }
+// QKV-epilogue arguments of one projection whose columns from vt_col0 on are
+// V (written transposed into vt) and whose columns before it are Q and/or K
+// (written into c, or as e4m3 codes into head slots of the QKV buffer's bytes
+// from qk8 on when the QK product is e4m3).
+GemmArgs qkv_args(siglip_model* m, const Gemm& g, const void* a, f16* c, void* vt, int vt_col0, uint8_t* qk8,
+                  int M) {
   GemmArgs args{};
   args.a = a;
   args.lda = m->width;
   args.w = g.w;
   args.ldw = g.k_pad;
-  args.c = qkv;
+  args.c = c;
   args.ldc = 3 * m->width;
   args.bias = g.bias;
   args.M = M;
@@ -401,17 +369,60 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* v
   args.acc_scale = m->acc_scale;
   args.out_scale = m->attn_fp8 ? m->attn_v_scale : m->op_scale;
   args.vt = static_cast<f16*>(vt);
-  args.vt_col0 = 2 * m->width;
+  args.vt_col0 = vt_col0;
   args.vt_tokens = m->tokens;
-  args.vt_heads = m->heads;
+  args.vt_heads = (g.n_pad - vt_col0) / m->head_dim;
   args.vt_dim = m->head_dim;
   args.vt_ld = m->tokens_pad;
   args.vt_inv_dim = 1.0f / (float)m->head_dim;
+  if (m->attn_qk8) {
+    args.qk8 = qk8;
+    args.qk8_ld = 6LL * m->width;  // bytes of one F16 row of the QKV buffer
+    args.qk8_pitch = kQK8SlotBytes;
+    args.qk8_scale = m->attn_v_scale;
+  }
+  return args;
+}
+
+// The fused QKV projection: Q and K row-major into qkv (or as e4m3 codes in
+// its bytes), V transposed per head into vt when the streaming attention is
+// used.
+void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* vt, int M, hipStream_t s) {
+  const Gemm& g = Ly.qkv;
+  const int W = m->width;
+  uint8_t* qk8 = reinterpret_cast<uint8_t*>(qkv);
+  if (m->separate_qkv) {
+    // Q and K into their columns of the fused row (or their e4m3 head slots);
+    // V as its own projection, transposed per head (all its columns are V)
+    if (m->attn_qk8) {
+      hip_check(launch_gemm(qkv_args(m, Ly.q, a, qkv, vt, W, qk8, M), EPI_QKV8, m->fp8, m->attn_fp8, s),
+                "q gemm launch");
+      hip_check(launch_gemm(qkv_args(m, Ly.k, a, qkv + W, vt, W, qk8 + (int64_t)m->heads * kQK8SlotBytes, M),
+                            EPI_QKV8, m->fp8, m->attn_fp8, s),
+                "k gemm launch");
+    } else {
+      gemm(m, Ly.q, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, Ly.k, a, W, M, qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    }
+    if (!m->vt_path) {
+      gemm(m, Ly.v, a, W, M, qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      return;
+    }
+    // c is not written: every column goes to vt
+    hip_check(launch_gemm(qkv_args(m, Ly.v, a, qkv + 2 * W, vt, 0, nullptr, M), EPI_QKV, m->fp8, m->attn_fp8, s),
+              "v gemm launch");
+    return;
+  }
+  if (!m->vt_path) {
+    gemm(m, g, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    return;
+  }
+  GemmArgs args = qkv_args(m, g, a, qkv, vt, 2 * W, qk8, M);
   // 3456-wide weight (4 MB e4m3, 8 MB F16) exceeds an XCD's L2 next to the
   // activations: walk tiles in bands of 8 row blocks (measured ~12% faster
   // at 46,656 rows than row-block-major order)
   args.group_m = 8;
-  hip_check(launch_gemm(args, EPI_QKV, m->fp8, m->attn_fp8, s), "qkv gemm launch");
+  hip_check(launch_gemm(args, m->attn_qk8 ? EPI_QKV8 : EPI_QKV, m->fp8, m->attn_fp8, s), "qkv gemm launch");
 }
 
 void capture(siglip_model* m, int stage, const void* src, size_t bytes, hipStream_t s) {
@@ -429,7 +440,16 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
     case SIGLIP_STAGE_EMBED: case SIGLIP_STAGE_H_ATTN: case SIGLIP_STAGE_H_OUT: break;
     case SIGLIP_STAGE_LN1: case SIGLIP_STAGE_ATTN: case SIGLIP_STAGE_LN2: b = e; break;
     case SIGLIP_STAGE_FINAL_LN: b = m->map_fold ? 2 : e; break;
-    case SIGLIP_STAGE_QKV: l = 3LL * m->width; c = m->vt_path ? 2LL * m->width : l; break;
+    case SIGLIP_STAGE_QKV:
+      if (m->attn_qk8) {  // e4m3 Q then K head slots, in the bytes of the F16 rows
+        l = 6LL * m->width;
+        c = 2LL * m->heads * kQK8SlotBytes;
+        b = 1;
+      } else {
+        l = 3LL * m->width;
+        c = m->vt_path ? 2LL * m->width : l;
+      }
+      break;
     case SIGLIP_STAGE_V_T:
       r = m->vt_path ? (int64_t)batch * m->heads * m->head_dim : 0;
       c = m->tokens;
@@ -532,13 +552,20 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
     if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, A.vt, cb(SIGLIP_STAGE_V_T), s);
     {
       LaunchTimer lt(m, SIGLIP_K_ATTENTION, s);
+      // Q and K: F16 columns of the QKV rows, or e4m3 head slots in their bytes
+      const uint8_t* qb8 = reinterpret_cast<const uint8_t*>(A.qkv);
+      const void* aq = m->attn_qk8 ? static_cast<const void*>(qb8) : A.qkv;
+      const void* ak = m->attn_qk8 ? static_cast<const void*>(qb8 + (int64_t)m->heads * kQK8SlotBytes)
+                                   : static_cast<const void*>(A.qkv + W);
+      const int64_t ald = m->attn_qk8 ? 6LL * W : 3LL * W;
+      const int apitch = m->attn_qk8 ? kQK8SlotBytes : 0;
       if (m->attn_fp8)
-        hip_check(launch_flash_attention_vt8(A.qkv, A.qkv + W, 3 * W, static_cast<const uint8_t*>(A.vt),
-                                             m->tokens_pad, A.o, W, B, m->heads, m->tokens, m->head_dim,
-                                             attn_scale, q8, m->op_scale, m->attn_v_scale, s),
+        hip_check(launch_flash_attention_vt8(aq, ak, ald, apitch, static_cast<const uint8_t*>(A.vt), m->tokens_pad,
+                                             A.o, W, B, m->heads, m->tokens, m->head_dim, attn_scale, q8,
+                                             m->op_scale, m->attn_v_scale, s),
                   "attention");
       else if (m->vt_path)
-        hip_check(launch_flash_attention_vt(A.qkv, A.qkv + W, 3 * W, static_cast<const f16*>(A.vt), m->tokens_pad,
+        hip_check(launch_flash_attention_vt(aq, ak, ald, apitch, static_cast<const f16*>(A.vt), m->tokens_pad,
                                             A.o, W, B, m->heads, m->tokens, m->head_dim, attn_scale, q8,
                                             m->op_scale, s),
                   "attention");
@@ -703,9 +730,9 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_INVALID_ARG, "separate_qkv must be 0 or 1");
   if (opt->map_explicit_kv != 0 && opt->map_explicit_kv != 1)
     return fail(SIGLIP_E_INVALID_ARG, "map_explicit_kv must be 0 or 1");
-  if (opt->attention_fp8 != 0 && opt->attention_fp8 != 1)
-    return fail(SIGLIP_E_INVALID_ARG, "attention_fp8 must be 0 or 1");
-  if (opt->attention_fp8 == 1 && (opt->fp8_scale_exp < -8 || opt->fp8_scale_exp > 8))
+  if (opt->attention_fp8 < 0 || opt->attention_fp8 > 3)
+    return fail(SIGLIP_E_INVALID_ARG, "attention_fp8 must be 0..3 (bit 0: PV product, bit 1: QK product)");
+  if (opt->attention_fp8 != 0 && (opt->fp8_scale_exp < -8 || opt->fp8_scale_exp > 8))
     return fail(SIGLIP_E_INVALID_ARG, "fp8_scale_exp must be in -8..8");
   if (blob_bytes < sizeof(BlobHeader)) return fail(SIGLIP_E_BAD_BLOB, "blob shorter than its 64-byte header");
   BlobHeader h;
@@ -798,8 +825,9 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->vt_path = flash_attention_vt_supported(m->head_dim);
     m->tokens_pad = (int)round_up(T, 64);
     m->separate_qkv = opt->separate_qkv == 1;
-    m->attn_fp8 = opt->attention_fp8 == 1;
-    if (m->attn_fp8 && !m->vt_path) {
+    m->attn_fp8 = (opt->attention_fp8 & 1) != 0;
+    m->attn_qk8 = (opt->attention_fp8 & 2) != 0;
+    if ((m->attn_fp8 || m->attn_qk8) && !m->vt_path) {
       delete m;
       return fail(SIGLIP_E_UNSUPPORTED, "attention_fp8 needs head_dim 64, 72 or 80");
     }
