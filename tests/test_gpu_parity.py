@@ -443,6 +443,27 @@ def test_c0_attention_fp8_stages_and_end_to_end(V, fp8, mode):
     np.testing.assert_array_equal(y.view(np.uint16), y2.view(np.uint16))
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2, 3], ids=["f16", "pv", "qk", "qk_pv"])
+@pytest.mark.parametrize("hd", [64, 80])
+def test_head_dims_64_and_80_stages_and_end_to_end(V, hd, mode):
+    """The streaming attention kernels at their other head widths (64: 18
+    heads of width 1152, explicit MAP K/V since the fold takes at most 16
+    heads; 80: 16 heads of width 1280), in every attention precision, stage
+    by stage and end to end at the single-layer F16 bar."""
+    dims = S.ModelDims(width=1152 if hd == 64 else 1280, heads=18 if hd == 64 else 16, head_dim=hd, depth=1)
+    _flush(f"head_dim {hd} attention_fp8={mode}")
+    model, wt = make_model(V, dims, 11, max_batch=2, attention_fp8=mode)
+    model.debug_capture(0)
+    x = S.make_pixels(dims, 2, 12)
+    y = run(model, x)
+    check_stages(model, wt, x, dims, False, 2, attn_fp8=mode)
+    ref = O.encode(wt, x, dims.heads)
+    cos, mx = per_image_metrics(y, ref)
+    _flush(f"  head_dim {hd} attention_fp8={mode}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    assert cos.min() >= 0.999 and mx.max() <= 2e-2
+    model.close()
+
+
 def test_c1_batch8_and_prefix_bitwise(V):
     cfg = S.CONFIGS["c1_1layer_b8_f16"]
     dims = S.SO400M.with_depth(1)
