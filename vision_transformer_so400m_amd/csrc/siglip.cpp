@@ -300,7 +300,7 @@ struct Acts {
   f16* my;
   void* ma;
   void* mu;
-  void* vt;  // F16, or e4m3 codes with attention_fp8
+  void* vt;  // F16, or e4m3 codes with the e4m3 PV product
   float* mscores;
   float* zbar;
 };
