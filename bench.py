@@ -59,12 +59,20 @@ def kernel_flops(cls, d, batch):
     }.get(cls)
 
 
+_COMMENT = re.compile(r'("(?:\\.|[^"\\])*")|//[^\n]*|/\*.*?\*/', re.S)
+
+
 def source_digest():
+    """Digest of the kernel and library sources with comments and blank
+    space removed, so that profiles taken on a source tree stay attached to
+    it across comment-only edits."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "vision_transformer_so400m_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = _COMMENT.sub(lambda m: m.group(1) or " ", fh.read())
+        code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+        h.update(f.encode() + code.encode())
     return h.hexdigest()[:16]
 
 
