@@ -336,10 +336,12 @@ def check_stages(model, wt, x, dims, fp8, batch, attn_fp8=0):
         vmax = np.abs(v4).max(axis=1)                                  # [batch, H, D]
         spread = vmax[:, None, :, :] + np.abs(ref_attn.reshape(batch, T, H, D))
         attn_extra = attn_extra + (2 * 2.0 ** -4 / (1 - 2.0 ** -4) * spread).reshape(M, W)
-    if fp8 and pv8:
+    if fp8:
+        # the attention band (R18 reading, plus the e4m3-probability term) can
+        # exceed one e4m3 step where outputs are small (subnormal codes are
+        # 2^-9 apart), so the code must lie within the band, not merely be a
+        # neighbour of the nearest
         e4m3_within("ATTN", st["ATTN"], ref_attn, se, band=attn_extra)
-    elif fp8:
-        e4m3_neighbours_ok("ATTN", st["ATTN"], ref_attn, se, band=attn_extra)
     else:
         assert_close("ATTN", st["ATTN"], ref_attn, extra=attn_extra)
     gemm_check("H_ATTN", f("ATTN"), "layer0.out.w", "layer0.out.b", add=f("EMBED"))
@@ -461,6 +463,35 @@ def test_head_dims_64_and_80_stages_and_end_to_end(V, hd, mode):
     cos, mx = per_image_metrics(y, ref)
     _flush(f"  head_dim {hd} attention_fp8={mode}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
     assert cos.min() >= 0.999 and mx.max() <= 2e-2
+    model.close()
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
+@pytest.mark.parametrize("tokens", [1, 65, 1025])
+def test_token_counts_degenerate_and_ragged(V, tokens, fp8):
+    """Other token counts through the whole path at batch 2 (two streams):
+    one token (every softmax has a single key and the MAP probe a single
+    token), 65 (one key past a 64-key block, one row past a 64-row GEMM
+    tile), 1025 (one key past sixteen blocks, one query past eight
+    128-query workgroups, and above the 1024 tokens of the folded MAP head,
+    so the explicit K/V projection runs). Stage by stage and end to end."""
+    dims = S.ModelDims(tokens=tokens, depth=1)
+    _flush(f"tokens {tokens} fp8={fp8}")
+    model, wt = make_model(V, dims, 13, max_batch=2, fp8=fp8)
+    model.debug_capture(0)
+    x = S.make_pixels(dims, 2, 14)
+    y = run(model, x)
+    check_stages(model, wt, x, dims, fp8, 2)
+    ref = O.encode(wt, x, dims.heads)
+    cos, mx = per_image_metrics(y, ref)
+    _flush(f"  tokens {tokens} fp8={fp8}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    if fp8:
+        assert cos.min() >= 0.99 and mx.max() <= 0.5
+    else:
+        assert cos.min() >= 0.999 and mx.max() <= 2e-2
+    model.debug_capture(-1)
+    y2 = run(model, x)
+    np.testing.assert_array_equal(y.view(np.uint16), y2.view(np.uint16))
     model.close()
 
 
