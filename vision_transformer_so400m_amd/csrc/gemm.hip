@@ -385,8 +385,8 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // Tile choice measured on the batch-64 shapes (M = 46,656): N divisible by
   // 256 takes 256x256 tiles of eight waves (128x64 each, one workgroup per
   // CU); the others take 128x128 tiles of eight waves (64x32 each) with two
-  // LDS stages, two workgroups per CU. Small M falls back to tiles that still
-  // fill the 256 CUs.
+  // LDS stages, two workgroups per CU. Small M falls back to smaller tiles
+  // that still fill the 256 CUs.
   const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
   if (tiles_128 >= 1024) {
     // Large grids walk tiles in bands of row blocks (tile_of) unless the
@@ -411,7 +411,13 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // x 4352, 6.0 -> 5.6 us for K = 1152; larger grids gain nothing from it).
   const long tiles_64 = (long)((g.M + 63) / 64) * (g.N / 64);
   if (tiles_64 < 512) return launch_cfg<64, 64, 32, 32, 4, FP8, EPI, OUT_FP8>(g, s);
-  return launch_cfg<64, 64, 32, 32, 3, FP8, EPI, OUT_FP8>(g, s);
+  // Between the two: 128x64 tiles of four waves (64x32 each), three stages.
+  // Measured with every launch reading its weights cold from HBM (as the
+  // layers of one small-batch call do), against 64x64 tiles with three
+  // stages: 729 x 4352 x 1152 14.5 -> 11.3 us, 729 x 3456 x 1152 10.4 ->
+  // 9.9 us, 2916 x 1152 x 4352 34.7 -> 24.7 us, 2916 x 1152 x 1152 12.6 ->
+  // 10.3 us.
+  return launch_cfg<128, 64, 64, 32, 3, FP8, EPI, OUT_FP8>(g, s);
 }
 
 template <bool FP8>
