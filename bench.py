@@ -97,12 +97,16 @@ def cpu_baseline(wt, pixels, heads):
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
+    # whole images, one call each, until about 10 s of wall time (at most 8)
     t0 = time.perf_counter()
-    O.encode(wt, pixels[:1], heads)
+    n = 0
+    while n < min(8, len(pixels)) and (n == 0 or time.perf_counter() - t0 < 10.0):
+        O.encode(wt, pixels[n:n + 1], heads)
+        n += 1
     dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 4), "unit": "images/sec", "cores": int(cores), "kind": "oracle",
-            "sample": "image 0 of the batch-64 input, 27 layers + MAP, float64 numpy oracle "
-                      f"(unquantized), {dt:.2f} s wall"}
+    return {"value": round(n / dt, 4), "unit": "images/sec", "cores": int(cores), "kind": "oracle",
+            "sample": f"images 0..{n - 1} of the batch-64 input, one call each, 27 layers + MAP, float64 "
+                      f"numpy oracle (unquantized), {dt:.2f} s wall"}
 
 
 def time_calls(model, x, out, steps, warmup=3):
