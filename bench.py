@@ -221,8 +221,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs the encoder on a single MI355X "
-              "(data-parallel sharding is described, not built). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the encoder on a single MI355X "
+              "(data-parallel sharding across GPUs is not implemented). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.sweep:

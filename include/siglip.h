@@ -34,7 +34,7 @@ typedef enum {
   SIGLIP_OK = 0,
   SIGLIP_E_INVALID_ARG = -1,   /* null pointer, size out of range, bad option */
   SIGLIP_E_BAD_BLOB = -2,      /* weight blob malformed, truncated or inconsistent */
-  SIGLIP_E_UNSUPPORTED = -3,   /* valid request this build cannot run (dims, device) */
+  SIGLIP_E_UNSUPPORTED = -3,   /* valid request this library cannot run (dims, device) */
   SIGLIP_E_OUT_OF_MEMORY = -4, /* device allocation failed */
   SIGLIP_E_HIP = -5            /* a HIP runtime call or kernel launch failed */
 } siglip_status;
@@ -113,7 +113,7 @@ typedef struct {
  * opt:        host pointer, read during the call.
  * out:        receives the new model; set to NULL on failure.
  * Errors: INVALID_ARG (null pointer, bad options), BAD_BLOB (checked on the
- * CPU before any HIP call), UNSUPPORTED (dims this build cannot run: width
+ * CPU before any HIP call), UNSUPPORTED (dims this library cannot run: width
  * != heads*head_dim, width % 128, head_dim > 80 or % 8, mlp % 8,
  * patch_dim % 4, tokens > 4096, or a device that is not gfx950),
  * OUT_OF_MEMORY, HIP. Blocks until the upload and conversion are complete.

@@ -801,7 +801,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
   e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("hipGetDeviceProperties: ") + hipGetErrorString(e));
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(SIGLIP_E_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", this build targets gfx950");
+    return fail(SIGLIP_E_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", the library is built for gfx950 only");
 
   siglip_model* m = new (std::nothrow) siglip_model();
   if (!m) return fail(SIGLIP_E_OUT_OF_MEMORY, "host allocation failed");
