@@ -128,10 +128,13 @@ def fp8_operand(x: np.ndarray, scale_exp: int = FP8_SCALE_EXP) -> np.ndarray:
 
 # ------------------------------------------------------------------ the model
 
-def _gemm(x, w, b, fp8: bool):
-    """A weight GEMM. In FP8 mode both operands are quantized to e4m3 at
-    scale 2^-4 first ([SLB] intro: "the host reference quantizes operands at
-    each selected GEMM"); accumulation and bias stay exact."""
+def weight_gemm(x, w, b, fp8: bool):
+    """A weight GEMM. In FP8 mode both operands are first replaced by their
+    e4m3 values at scale 2^-4 ([SLB] intro, FP8 paragraph: the pages' host
+    reference applies the same operand quantization at every GEMM it checks);
+    the products, their sum and the bias stay exact. Pinned exactly against
+    torch's float8_e4m3fn casts composed by hand, a hand-worked case at
+    rounding midpoints and saturation, and an independent torch model."""
     if fp8:
         return linear(fp8_operand(x), fp8_operand(w), b)
     return linear(x, w, b)
@@ -141,7 +144,7 @@ def patch_embed(x: np.ndarray, wt: Dict[str, np.ndarray], fp8: bool = False) -> 
     """[SLB] intro: the VALID 14x14/14 patch convolution is the 588->width
     embedding GEMM plus bias on patch-ordered pixels, then the learned
     positional embedding is added per token."""
-    return _gemm(x, wt["embed.w"], wt["embed.b"], fp8) + wt["pos"]
+    return weight_gemm(x, wt["embed.w"], wt["embed.b"], fp8) + wt["pos"]
 
 
 def encoder_layer(h: np.ndarray, wt: Dict[str, np.ndarray], i: int, heads: int,
@@ -154,14 +157,14 @@ def encoder_layer(h: np.ndarray, wt: Dict[str, np.ndarray], i: int, heads: int,
     w = h.shape[-1]
     d = w // heads
     a = layer_norm(h, wt[p + "ln1.g"], wt[p + "ln1.b"])
-    qkv = _gemm(a, wt[p + "qkv.w"], wt[p + "qkv.b"], fp8)
+    qkv = weight_gemm(a, wt[p + "qkv.w"], wt[p + "qkv.b"], fp8)
     q, k, v = qkv[..., :w], qkv[..., w:2 * w], qkv[..., 2 * w:]
     o = merge_heads(attention(split_heads(q, heads), split_heads(k, heads),
                               split_heads(v, heads), 1.0 / math.sqrt(d)))
-    h1 = h + _gemm(o, wt[p + "out.w"], wt[p + "out.b"], fp8)
+    h1 = h + weight_gemm(o, wt[p + "out.w"], wt[p + "out.b"], fp8)
     a2 = layer_norm(h1, wt[p + "ln2.g"], wt[p + "ln2.b"])
-    u = gelu_tanh(_gemm(a2, wt[p + "mlp1.w"], wt[p + "mlp1.b"], fp8))
-    h2 = h1 + _gemm(u, wt[p + "mlp2.w"], wt[p + "mlp2.b"], fp8)
+    u = gelu_tanh(weight_gemm(a2, wt[p + "mlp1.w"], wt[p + "mlp1.b"], fp8))
+    h2 = h1 + weight_gemm(u, wt[p + "mlp2.w"], wt[p + "mlp2.b"], fp8)
     if stages is not None:
         stages.update({p + "ln1": a, p + "qkv": qkv, p + "attn": o,
                        p + "h_attn": h1, p + "ln2": a2, p + "mlp_hidden": u,
@@ -178,16 +181,16 @@ def map_head(z: np.ndarray, wt: Dict[str, np.ndarray], heads: int,
     out = y + MLP(LN(y)). Returns [B, 1, width] (the probe axis is kept)."""
     w = z.shape[-1]
     d = w // heads
-    q = _gemm(wt["map.probe"], wt["map.q.w"], wt["map.q.b"], fp8)    # [1, W]
-    kv = _gemm(z, wt["map.kv.w"], wt["map.kv.b"], fp8)               # [B, T, 2W]
+    q = weight_gemm(wt["map.probe"], wt["map.q.w"], wt["map.q.b"], fp8)    # [1, W]
+    kv = weight_gemm(z, wt["map.kv.w"], wt["map.kv.b"], fp8)               # [B, T, 2W]
     k, v = kv[..., :w], kv[..., w:]
     qh = split_heads(np.broadcast_to(q, (z.shape[0], 1, w)), heads)  # [B,H,1,D]
     o = merge_heads(attention(qh, split_heads(k, heads), split_heads(v, heads),
                               1.0 / math.sqrt(d)))                   # [B,1,W]
-    y = _gemm(o, wt["map.out.w"], wt["map.out.b"], fp8)
+    y = weight_gemm(o, wt["map.out.w"], wt["map.out.b"], fp8)
     a = layer_norm(y, wt["map.ln.g"], wt["map.ln.b"])
-    u = gelu_tanh(_gemm(a, wt["map.mlp1.w"], wt["map.mlp1.b"], fp8))
-    out = y + _gemm(u, wt["map.mlp2.w"], wt["map.mlp2.b"], fp8)
+    u = gelu_tanh(weight_gemm(a, wt["map.mlp1.w"], wt["map.mlp1.b"], fp8))
+    out = y + weight_gemm(u, wt["map.mlp2.w"], wt["map.mlp2.b"], fp8)
     if stages is not None:
         stages.update({"map.q": q, "map.kv": kv, "map.attn": o, "map.y": y,
                        "map.ln": a, "map.mlp_hidden": u, "out": out})

@@ -299,12 +299,93 @@ def test_fp32_arithmetic_agrees_with_fp64():
     assert np.abs(y64 - y32).max() < 1e-4
 
 
-def test_fp8_mode_error_scale():
-    # quantizing every weight-GEMM operand to e4m3 moves the output by the
-    # order the pages report for their FP8 runs (max abs error ~0.1 for one
-    # layer), not by orders of magnitude more or less
-    dims = S.SO400M.with_depth(1)
-    wt = S.make_weights(dims, seed=0)
-    x = S.make_pixels(dims, 1, seed=0)
-    d = np.abs(O.encode(wt, x, 16, fp8=True) - O.encode(wt, x, 16)).max()
-    assert 1e-3 < d < 0.5
+def _torch_e4m3_operand(a):
+    """Independent e4m3 operand value: torch's float8_e4m3fn cast (round to
+    nearest even) of 2^4 a after clipping to +-448 (torch gives NaN above the
+    range instead of saturating), divided back by 2^4."""
+    a = torch.as_tensor(np.asarray(a, np.float64))
+    return torch.clamp(a * 16.0, -448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float64) / 16.0
+
+
+def test_fp8_gemm_equals_scaled_code_product():
+    # float32 inputs, so 2^4 x is exact and there is no double rounding on
+    # torch's side; a few values past the e4m3 range exercise saturation
+    x = (RNG.standard_normal((5, 64)) * 0.5).astype(np.float32)
+    w = (RNG.standard_normal((64, 7)) * 0.05).astype(np.float32)
+    x[0, :3] = [40.0, -35.0, 1e-5]
+    b = RNG.standard_normal(7)
+    y = O.weight_gemm(x.astype(np.float64), w.astype(np.float64), b, True)
+    cx = torch.clamp(torch.from_numpy(x.astype(np.float64)) * 16, -448, 448).to(torch.float8_e4m3fn)
+    cw = torch.clamp(torch.from_numpy(w.astype(np.float64)) * 16, -448, 448).to(torch.float8_e4m3fn)
+    ref = (cx.to(torch.float64).numpy() @ cw.to(torch.float64).numpy()) / 256.0 + b
+    np.testing.assert_array_equal(y, ref)
+    # quantizing only the weights, or quantizing without the 2^4 scale,
+    # gives other numbers
+    assert not np.array_equal(O.linear(x.astype(np.float64), O.fp8_operand(w), b), ref)
+    unscaled = (torch.from_numpy(x.astype(np.float64)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+                @ torch.from_numpy(w.astype(np.float64)).to(torch.float8_e4m3fn).to(torch.float64).numpy()) + b
+    assert not np.allclose(unscaled, ref, rtol=1e-3, atol=1e-6)
+
+
+def test_fp8_gemm_hand_worked_midpoints_and_saturation():
+    # 2^4 x = [[1.0625, 1.1875], [500, -0.016]]: 1.0625 is the midpoint of
+    # 1 and 1.125 (ties to the even mantissa: 1), 1.1875 the midpoint of
+    # 1.125 and 1.25 (even: 1.25), 500 saturates to 448, -0.016 is
+    # -8.192 subnormal steps of 2^-9 -> -8 * 2^-9 = -0.015625.
+    # 2^4 w = [[2, 0.5], [1, 3]] are e4m3 values.
+    x = np.array([[1.0625, 1.1875], [500.0, -0.016]]) / 16
+    w = np.array([[2.0, 0.5], [1.0, 3.0]]) / 16
+    b = np.array([0.5, -0.25])
+    # codes product [[1*2 + 1.25*1, 1*0.5 + 1.25*3], [448*2 - 0.015625, 448*0.5 - 0.015625*3]]
+    #             = [[3.25, 4.25], [895.984375, 223.953125]], times 2^-8, plus b
+    expect = np.array([[3.25, 4.25], [895.984375, 223.953125]]) / 256 + b
+    np.testing.assert_array_equal(O.weight_gemm(x, w, b, True), expect)
+    assert expect[0, 0] == 0.5126953125 and expect[1, 1] == 0.62481689453125
+
+
+def _torch_fp8_model(wt, pixels, dims, layers):
+    """Independent float64 model in which every weight GEMM (patch, QKV,
+    out-projection, MLP, MAP q, K/V, out-projection and MLP) multiplies torch
+    e4m3 casts of both operands; attention, layernorm, GELU and residuals
+    exact. Works on patch vectors."""
+    W, H, D = dims.width, dims.heads, dims.head_dim
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    q8 = _torch_e4m3_operand
+
+    def lin(a, wn, bn):
+        return q8(a) @ q8(wt[wn]) + t(wt[bn])
+
+    def heads_attn(q, k, v):
+        B, Tq, Tk = q.shape[0], q.shape[1], k.shape[1]
+        qh = q.reshape(B, Tq, H, D).transpose(1, 2)
+        kh = k.reshape(B, Tk, H, D).transpose(1, 2)
+        vh = v.reshape(B, Tk, H, D).transpose(1, 2)
+        p = torch.softmax(qh @ kh.transpose(-1, -2) / math.sqrt(D), dim=-1)
+        return (p @ vh).transpose(1, 2).reshape(B, Tq, W)
+
+    ln = lambda a, p: F.layer_norm(a, (W,), t(wt[p + ".g"]), t(wt[p + ".b"]), eps=1e-6)
+    gelu = lambda a: F.gelu(a, approximate="tanh")
+    x = lin(t(pixels), "embed.w", "embed.b") + t(wt["pos"])
+    for i in range(layers):
+        p = f"layer{i}."
+        qkv = lin(ln(x, p + "ln1"), p + "qkv.w", p + "qkv.b")
+        o = heads_attn(qkv[..., :W], qkv[..., W:2 * W], qkv[..., 2 * W:])
+        x = x + lin(o, p + "out.w", p + "out.b")
+        x = x + lin(gelu(lin(ln(x, p + "ln2"), p + "mlp1.w", p + "mlp1.b")), p + "mlp2.w", p + "mlp2.b")
+    z = ln(x, "final_ln")
+    q = lin(t(wt["map.probe"]), "map.q.w", "map.q.b").expand(z.shape[0], 1, W)
+    kv = lin(z, "map.kv.w", "map.kv.b")
+    y = lin(heads_attn(q, kv[..., :W], kv[..., W:]), "map.out.w", "map.out.b")
+    return (y + lin(gelu(lin(ln(y, "map.ln"), "map.mlp1.w", "map.mlp1.b")), "map.mlp2.w", "map.mlp2.b")).numpy()
+
+
+@pytest.mark.parametrize("dims", [S.small_dims(2), S.four_token_dims(2)],
+                         ids=["small_w144_t4", "fourtoken_w1152"])
+def test_fp8_whole_model_matches_torch_e4m3_model(dims):
+    wt = S.make_weights(dims, seed=8)
+    x = S.make_pixels(dims, 2, seed=9)
+    ours = O.encode(wt, x, dims.heads, fp8=True)
+    ref = _torch_fp8_model(wt, x, dims, dims.depth)
+    np.testing.assert_allclose(ours, ref, rtol=1e-9, atol=1e-10)
+    # and it is not the unquantized model
+    assert np.abs(ours - O.encode(wt, x, dims.heads)).max() > 1e-3
