@@ -13,8 +13,9 @@ pass with HIP events around every launch, the roofline of the dominant
 kernel from a second timed pass of the same calls with events around that
 class's launches (launch events make the library run the batch unsplit on
 one stream, so every launch covers the whole batch and its duration is the
-kernel's own), and a CPU baseline (the float64 oracle on a one-image sample
-on the host cores).
+kernel's own), the attention workload alone ([32, 729, 16 x 72]) against its
+MFMA and HBM floors, the F16 27-layer latency at batch 1 and 2, and a CPU
+baseline (the FP32 oracle on whole images of the input, on the host cores).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -36,12 +37,20 @@ PEAK = {  # MI355X dense peaks
 }
 
 
-def algorithmic_flops_per_image(d, layers):
-    """Unpadded multiply-add count x2 of one image's forward pass."""
+def algorithmic_flops_per_image(d, layers, map_fold=True):
+    """Unpadded multiply-add count x2 of one image's forward pass, for the
+    MAP head the library runs: folded (default) = scores Z . u_h and the
+    probability-weighted sum of Z for each head (2 T W H each) plus the W_v
+    product (2 W^2); explicit = the K/V GEMM (2 T W 2W) plus the probe
+    attention (4 H T D). Both add the output projection and the MLP."""
     T, W, F, P, H, D = d.tokens, d.width, d.mlp, d.patch_dim, d.heads, d.head_dim
     embed = 2 * T * P * W
     layer = 2 * T * W * 3 * W + 4 * H * T * T * D + 2 * T * W * W + 2 * 2 * T * W * F
-    map_head = 2 * T * W * 2 * W + 4 * H * T * D + 2 * W * W + 2 * 2 * W * F
+    if map_fold:
+        map_kv_attn = 2 * T * W * H + 2 * H * T * W + 2 * W * W
+    else:
+        map_kv_attn = 2 * T * W * 2 * W + 4 * H * T * D
+    map_head = map_kv_attn + 2 * W * W + 2 * 2 * W * F
     return embed + layers * layer + map_head
 
 
@@ -91,22 +100,89 @@ def profiled_traffic(kernel_class):
 
 
 def cpu_baseline(wt, pixels, heads):
+    """The FP32 oracle (numpy, float32 arithmetic) on whole images of the
+    batch-64 input, one call each, until about 10 s have passed, with the
+    BLAS thread pool set to the CPUs this process may run on."""
+    import numpy as np
+
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
-    # whole images, one call each, until about 10 s of wall time (at most 8)
-    t0 = time.perf_counter()
-    n = 0
-    while n < min(8, len(pixels)) and (n == 0 or time.perf_counter() - t0 < 10.0):
-        O.encode(wt, pixels[n:n + 1], heads)
-        n += 1
-    dt = time.perf_counter() - t0
+        limiter = None
+    try:
+        t0 = time.perf_counter()
+        n = 0
+        while n < min(8, len(pixels)) and (n == 0 or time.perf_counter() - t0 < 10.0):
+            O.encode(wt, pixels[n:n + 1], heads, dtype=np.float32)
+            n += 1
+        dt = time.perf_counter() - t0
+    finally:
+        if limiter is not None:
+            limiter.unregister()
     return {"value": round(n / dt, 4), "unit": "images/sec", "cores": int(cores), "kind": "oracle",
-            "sample": f"images 0..{n - 1} of the batch-64 input, one call each, 27 layers + MAP, float64 "
-                      f"numpy oracle (unquantized), {dt:.2f} s wall"}
+            "sample": f"images 0..{n - 1} of the batch-64 input, one call each, 27 layers + MAP, FP32 "
+                      f"numpy oracle (unquantized), {cores} BLAS threads, {dt:.2f} s wall"}
+
+
+def attention_alone(V, steps=30):
+    """The attention workload alone: [32, 729, 16 x 72] F16 Q, K, V from N(0,1)
+    (seeds (0,2..4)), scale 1/sqrt(72), through siglip_attention (V transposed
+    per image, then the encoder's streaming kernel); HIP events around each
+    call on the current stream, median of `steps` calls after 5 warm-up."""
+    import numpy as np
+    import torch
+
+    import synthetic as S
+    cfg = S.CONFIGS["c2_attention_b32"]
+    b, t, h, d = cfg["batch"], cfg["tokens"], cfg["heads"], cfg["head_dim"]
+    q, k, v = (torch.from_numpy(a).cuda() for a in S.make_attention_inputs(b, t, h, d, cfg["seeds"]))
+    out = torch.empty((b, t, h * d), dtype=torch.float16, device="cuda")
+    scale = 1.0 / d ** 0.5
+    for _ in range(5):
+        V.attention(q, k, v, h, d, scale, out=out)
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        V.attention(q, k, v, h, d, scale, out=out)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times))
+    flops = 4 * b * h * t * t * d
+    hbm = 4 * b * t * h * d * 2
+    mfma_floor = flops / (PEAK["f16_mfma_tflops"] * 1e12) * 1e6
+    hbm_floor = hbm / (PEAK["hbm_gbs"] * 1e9) * 1e6
+    return {"workload": "attention alone, batch 32 x 16 heads, T=729, head dim 72, F16",
+            "us_median": round(us, 2), "calls": steps, "tflops": round(flops / us / 1e6, 1),
+            "mfma_floor_us": round(mfma_floor, 1), "hbm_floor_us": round(hbm_floor, 1),
+            "frac_of_mfma_floor": round(mfma_floor / us, 3), "frac_of_hbm_floor": round(hbm_floor / us, 3),
+            "includes": "the V transpose into the staging buffer and the attention kernel"}
+
+
+def f16_latency(V, steps):
+    """Latency of the 27-layer model with F16 GEMM operands (weights and
+    pixels seed 1) at batch 1 and 2."""
+    import torch
+
+    import synthetic as S
+    d = S.SO400M
+    wt = S.make_weights(d, 1)
+    model = V.Model(S.pack_blob(d, wt), max_batch=2, fp8=False)
+    del wt
+    x = torch.from_numpy(S.make_pixels(d, 2, 1)).cuda()
+    res = {"workload": "27 layers + MAP, F16 GEMM operands, seed 1"}
+    for b in (1, 2):
+        xb = x[:b].contiguous()
+        o = torch.empty((b, 1, d.width), dtype=torch.float16, device="cuda")
+        ms = time_calls(model, xb, o, steps, warmup=5)
+        res[f"b{b}"] = {"ms": round(ms, 4), "images_per_s": round(b / ms * 1e3, 2)}
+    model.close()
+    return res
 
 
 def time_calls(model, x, out, steps, warmup=3):
@@ -298,7 +374,7 @@ def main():
     model.debug_timing(False)
     deterministic = deterministic and bool(torch.equal(out.view(torch.int16), ref_bits.view(torch.int16)))
 
-    flops_img = algorithmic_flops_per_image(d, d.depth)
+    flops_img = algorithmic_flops_per_image(d, d.depth, map_fold=True)
     value = B / (ms_per_step / 1e3)
     tflops = flops_img * B / (ms_per_step / 1e3) / 1e12
     avg_s = ms_dom / n_dom / 1e3
@@ -321,6 +397,10 @@ def main():
         model.encode(x1, out=o1)
     torch.cuda.synchronize()
     b1_ms = (time.perf_counter() - t0) * 1e3 / args.b1_steps
+    model.close()
+    del x, out
+    c2 = attention_alone(V)
+    c3 = f16_latency(V, args.b1_steps)
 
     line = {
         "metric": "images/sec, SigLIP So400m/14 378px 27-layer at B=1 and B=64; % MFMA peak",
@@ -333,7 +413,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 GEMM operands (f32 accumulate), f16 attention/layernorm/residuals",
+        "dtype": "fp8_e4m3 GEMM operands (f32 accumulate), f16 attention/layernorm/residuals; "
+                 "MAP K/V folded (f16 Z, f32 accumulate)",
         "data": "synthetic (seeded N(0,1) patch vectors, Gaussian-Xavier weights, seed 2)",
         "config": {"workload": "SigLIP So400m/14 378px image encoder, 27 layers + MAP head, batch 64, "
                                "e4m3 GEMM operands at scale 2^-4",
@@ -347,13 +428,13 @@ def main():
         "deterministic_across_steps": deterministic,
         "b1": {"ms": round(b1_ms, 4), "images_per_s": round(1e3 / b1_ms, 2),
                "workload": "same model and weights, batch 1"},
+        "f16_27layer_latency": c3,
+        "attention_b32_t729": c2,
         "kernels": kernels,
         "roofline": roofline,
         "context": {"ipu_27layer_b1_images_per_s": 110.4, "ipu_27layer_b2_images_per_s": 126.1,
                     "note": "Graphcore IPU figures from the pages (FP8 projections), another machine"},
     }
-    model.close()
-    del x, out
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wt, pixels, d.heads)
     else:

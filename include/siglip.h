@@ -139,8 +139,8 @@ SIGLIP_API int siglip_create(const void* blob, size_t blob_bytes,
  * before its later work, so the call behaves as one ordered unit of
  * hip_stream. Images are independent, each output row is computed by the
  * same kernels in the same order either way, and the results are bitwise
- * identical. Stage capture and launch timing (siglip_debug_*) run the batch
- * on hip_stream alone.
+ * identical. Launch timing (siglip_debug_timing) and, in the test build,
+ * stage capture run the batch on hip_stream alone.
  * The model's workspace is shared by its calls: calls on one model must be
  * ordered (one stream, or explicit synchronisation). Results are bitwise
  * deterministic run to run. The call enqueues kernel launches and event
@@ -169,7 +169,16 @@ SIGLIP_API int siglip_encode(siglip_model* m, const void* pixels_f16,
  * Requires head_dim % 8 == 0, head_dim <= 80, row_stride_elems % 8 == 0
  * and >= heads*head_dim, 16-byte aligned pointers, tokens >= 1. No data
  * past token tokens-1 of an image or past column head_dim-1 of a head is
- * read. Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ * read.
+ * Head widths 64, 72 and 80 run the encoder's own streaming kernel: V is
+ * first transposed per image into a staging buffer of
+ * batch * heads*head_dim * round_up(tokens, 64) * 2 bytes that the library
+ * owns, one per device, allocated by the first call that needs more than
+ * any call before it (hipMalloc; that call is then not capturable into a
+ * HIP graph) and kept until the process ends. Calls on one device share
+ * it: calls that overlap in time on one device (different streams, no
+ * ordering) race. Other head widths use a register-staged kernel and no
+ * staging. Errors: INVALID_ARG, UNSUPPORTED, OUT_OF_MEMORY, HIP.
  */
 SIGLIP_API int siglip_attention(const void* q, const void* k, const void* v,
                                 int64_t row_stride_elems, void* o,
@@ -195,68 +204,9 @@ SIGLIP_API int siglip_model_info(const siglip_model* m, int32_t* width,
                                  int32_t* max_batch, int32_t* gemm_precision);
 
 /* ---------------------------------------------------------------------
- * Diagnostics: per-stage checkpoints, the analogue of the operator
- * checkpoints the pages validate against a host reference (page
- * "Single-layer SigLIP vision benchmark", "Performance follow-up": 40
- * operator checkpoints). Not needed for inference.
+ * Measurement: per-launch timing of the kernel classes of siglip_encode
+ * (used by the benchmark for per-kernel times and the roofline figure).
  * ------------------------------------------------------------------- */
-typedef enum {
-  SIGLIP_STAGE_EMBED = 0,      /* [M, width]   F16  patch GEMM + bias + pos   */
-  SIGLIP_STAGE_LN1 = 1,        /* [M, width]   F16 | e4m3 code (FP8 mode)     */
-  SIGLIP_STAGE_QKV = 2,        /* [M, 3*width] F16                            */
-  SIGLIP_STAGE_ATTN = 3,       /* [M, width]   F16 | e4m3 code                */
-  SIGLIP_STAGE_H_ATTN = 4,     /* [M, width]   F16  after attention residual  */
-  SIGLIP_STAGE_LN2 = 5,        /* [M, width]   F16 | e4m3 code                */
-  SIGLIP_STAGE_MLP_HIDDEN = 6, /* [M, mlp_pad] F16 | e4m3 code (post-GELU)    */
-  SIGLIP_STAGE_H_OUT = 7,      /* [M, width]   F16  after MLP residual        */
-  SIGLIP_STAGE_FINAL_LN = 8,   /* [M, width]   F16 | e4m3 code (F16 whenever
-                                  the MAP K/V projection is folded)           */
-  SIGLIP_STAGE_MAP_KV = 9,     /* [M, 2*width] F16 (explicit MAP K/V only;
-                                  0 rows when folded)                         */
-  SIGLIP_STAGE_MAP_ATTN = 10,  /* [B, width]   F16 | e4m3 code                */
-  SIGLIP_STAGE_MAP_Y = 11,     /* [B, width]   F16  MAP output projection     */
-  SIGLIP_STAGE_MAP_LN = 12,    /* [B, width]   F16 | e4m3 code                */
-  SIGLIP_STAGE_MAP_HIDDEN = 13,/* [B, mlp_pad] F16 | e4m3 code (post-GELU)    */
-  SIGLIP_STAGE_MAP_Q = 14,     /* [1, width]   F16  probe query (create time) */
-  SIGLIP_STAGE_V_T = 15,       /* [B*heads*head_dim, round_up(tokens,64)] F16
-                                  (e4m3 codes of v * 2^-fp8_scale_exp with
-                                  the e4m3 PV product): V of each (image,
-                                  head) transposed (dims x tokens, zeros past
-                                  tokens); when present, the QKV stage holds
-                                  only the Q and K columns; with the e4m3 QK
-                                  product the QKV stage is [M, 2*heads*80]
-                                  e4m3 codes, head slots of 80 bytes (Q heads,
-                                  then K heads; bytes head_dim..79 of a slot
-                                  unused), row stride 6*width bytes           */
-  SIGLIP_STAGE_COUNT = 16
-} siglip_stage;
-
-/* Capture stage outputs on later siglip_encode calls: layer-local stages
- * (LN1..H_OUT) of encoder layer `layer` (0-based) and every other stage.
- * layer < 0 turns capture off. Allocates the capture buffers (sized for
- * max_batch) on first use. Errors: INVALID_ARG, OUT_OF_MEMORY. */
-SIGLIP_API int siglip_debug_capture(siglip_model* m, int32_t layer);
-
-/* Describe a captured stage of the last capturing encode: rows, columns
- * holding data, row stride in elements and bytes per element (2 = F16,
- * 1 = e4m3 code of x * 2^-fp8_scale_exp). Any pointer may be NULL. */
-SIGLIP_API int siglip_debug_stage_info(const siglip_model* m, int32_t stage,
-                                       int64_t* rows, int64_t* cols,
-                                       int64_t* ld, int32_t* elem_bytes);
-
-/* Copy a captured stage (rows*ld*elem_bytes bytes) to host memory dst of
- * dst_bytes; synchronises the device. Errors: INVALID_ARG (capture off,
- * stage out of range, dst too small), HIP. */
-SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage,
-                                  void* dst, size_t dst_bytes);
-
-/* Fill the whole workspace (every activation buffer, including row and
- * column padding) with a 16-bit pattern, e.g. 0x7E00 (F16 NaN), to show
- * that siglip_encode never reads data it did not write in the same call
- * (page "Layout and barrier diagnosis", "Padding, SRAM placement and paired
- * transfers": padding is read, so unwritten tails must not be). Synchronous. */
-SIGLIP_API int siglip_debug_fill_workspace(siglip_model* m, uint16_t pattern);
-
 /* Kernel classes of one siglip_encode call, for per-launch timing. */
 typedef enum {
   SIGLIP_K_INPUT = 0,       /* patch rows -> padded GEMM operand          */

@@ -8,6 +8,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+# Tests run against the test build of the library (libsiglip_test.so: the
+# product library plus the stage-capture and workspace-poisoning hooks of
+# include/siglip_test_hooks.h); checks of the product build load
+# libsiglip.so explicitly by path.
+import vision_transformer_so400m_amd as _V  # noqa: E402
+
+_V.use_test_hooks()
+
+
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs a real MI355X (gfx950) and the built HIP library")

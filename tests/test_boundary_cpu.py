@@ -1,7 +1,8 @@
-"""C-ABI boundary checks that need no GPU: the library loads, exports every
-function include/siglip.h declares, and rejects malformed blobs, unsupported
-dimensions, bad options and null pointers with the documented status before
-any HIP call."""
+"""C-ABI boundary checks that need no GPU: the product library loads and
+exports every function include/siglip.h declares (and none of the test
+hooks), the test build also exports those of include/siglip_test_hooks.h,
+and both reject malformed blobs, unsupported dimensions, bad options and null
+pointers with the documented status before any HIP call."""
 import ctypes
 import os
 import re
@@ -15,22 +16,38 @@ import vision_transformer_so400m_amd as V
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "siglip.h")
+HOOKS_HEADER = os.path.join(ROOT, "include", "siglip_test_hooks.h")
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(path=HEADER):
+    text = open(path).read()
     return sorted(set(re.findall(r"SIGLIP_API\s+[\w\s\*]+?\b(siglip_\w+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
     assert _declared() == sorted(V.EXPORTED)
+    assert _declared(HOOKS_HEADER) == sorted(V.TEST_HOOKS)
 
 
-def test_library_exports_every_declared_symbol():
-    lib = V.load_library()
+def _exports(lib, name):
+    try:
+        return bool(ctypes.cast(getattr(lib, name), ctypes.c_void_p).value)
+    except AttributeError:
+        return False
+
+
+def test_product_library_exports_every_declared_symbol_and_no_hook():
+    lib = V.load_library(V.LIB_PATH)
     for name in _declared():
-        assert hasattr(lib, name), name
-        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+        assert _exports(lib, name), name
+    for name in _declared(HOOKS_HEADER):
+        assert not _exports(lib, name), name
+
+
+def test_test_library_exports_the_hooks_too():
+    lib = V.load_library(V.TEST_LIB_PATH)
+    for name in _declared() + _declared(HOOKS_HEADER):
+        assert _exports(lib, name), name
 
 
 def test_status_strings():
@@ -182,8 +199,12 @@ def test_null_pointers_and_bad_attention_args():
 
 def test_e4m3_decode_helper_matches_oracle_rounding():
     import oracle as O
+    from e4m3_codes import e4m3_decode
     codes = np.arange(256, dtype=np.uint8)
-    vals = V.e4m3_decode(codes, scale_exp=0)
+    vals = e4m3_decode(codes, scale_exp=0)
     finite = ~np.isnan(vals)
     assert finite.sum() == 254
     np.testing.assert_array_equal(O.e4m3_round(vals[finite]), vals[finite])
+    # a few codes decoded by hand: 0x38 = 1.0, 0x7E = 448, 0x01 = 2^-9, 0xB8 = -1.0
+    np.testing.assert_array_equal(e4m3_decode(np.array([0x38, 0x7E, 0x01, 0xB8], np.uint8), 0),
+                                  [1.0, 448.0, 2.0 ** -9, -1.0])

@@ -14,6 +14,7 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsiglip.so")
+TEST_LIB_PATH = os.path.join(_PKG, "libsiglip_test.so")   # + include/siglip_test_hooks.h
 
 SIGLIP_OK = 0
 SIGLIP_E_INVALID_ARG = -1
@@ -28,8 +29,9 @@ STAGE = {n: i for i, n in enumerate(STAGES)}
 
 EXPORTED = ["siglip_create", "siglip_encode", "siglip_attention", "siglip_destroy",
             "siglip_status_string", "siglip_last_error", "siglip_model_info",
-            "siglip_debug_capture", "siglip_debug_stage_info", "siglip_debug_stage",
-            "siglip_debug_fill_workspace", "siglip_debug_timing", "siglip_debug_timing_read"]
+            "siglip_debug_timing", "siglip_debug_timing_read"]
+TEST_HOOKS = ["siglip_debug_capture", "siglip_debug_stage_info", "siglip_debug_stage",
+              "siglip_debug_fill_workspace"]
 
 KERNEL_CLASSES = ["INPUT", "EMBED", "LAYERNORM", "QKV", "ATTENTION", "OUT_PROJ", "MLP_UP",
                   "MLP_DOWN", "MAP_KV", "MAP_ATTENTION", "MAP_TAIL"]
@@ -51,17 +53,35 @@ class siglip_options(ctypes.Structure):
 
 
 _lib: Optional[ctypes.CDLL] = None
+_path = LIB_PATH
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libsiglip.so (built in-tree by build.build()); raises if absent."""
+def use_test_hooks() -> None:
+    """Load the test build (libsiglip_test.so: the product library plus the
+    stage-capture and workspace-poisoning hooks) instead of libsiglip.so.
+    Must be called before the library is first loaded in this process."""
+    global _path
+    if _lib is not None and _path != TEST_LIB_PATH:
+        raise RuntimeError("the product library is already loaded in this process")
+    _path = TEST_LIB_PATH
+
+
+def has_test_hooks() -> bool:
+    return _path == TEST_LIB_PATH
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the library (built in-tree by build.build()); raises if absent.
+    Without a path: libsiglip.so, or libsiglip_test.so after use_test_hooks().
+    With a path: that file, loaded on its own (not cached)."""
     global _lib
-    if _lib is not None:
+    if path is None and _lib is not None:
         return _lib
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with "
+    p = path or _path
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with "
                            "`python -m vision_transformer_so400m_amd.build` (no CPU fallback exists)")
-    lib = ctypes.CDLL(path)
+    lib = ctypes.CDLL(p)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     P = ctypes.POINTER
     lib.siglip_create.argtypes = [vp, ctypes.c_size_t, P(siglip_options), P(vp)]
@@ -73,15 +93,27 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.siglip_last_error.argtypes = []
     lib.siglip_last_error.restype = ctypes.c_char_p
     lib.siglip_model_info.argtypes = [vp] + [P(i32)] * 9
-    lib.siglip_debug_capture.argtypes = [vp, i32]
-    lib.siglip_debug_stage_info.argtypes = [vp, i32, P(i64), P(i64), P(i64), P(i32)]
-    lib.siglip_debug_stage.argtypes = [vp, i32, vp, ctypes.c_size_t]
-    lib.siglip_debug_fill_workspace.argtypes = [vp, ctypes.c_uint16]
     lib.siglip_debug_timing.argtypes = [vp, ctypes.c_uint32]
     lib.siglip_debug_timing_read.argtypes = [vp, i32, P(ctypes.c_double), P(i64)]
-    for name in EXPORTED:
+    names = list(EXPORTED)
+    if hasattr(lib, "siglip_debug_capture"):
+        lib.siglip_debug_capture.argtypes = [vp, i32]
+        lib.siglip_debug_stage_info.argtypes = [vp, i32, P(i64), P(i64), P(i64), P(i32)]
+        lib.siglip_debug_stage.argtypes = [vp, i32, vp, ctypes.c_size_t]
+        lib.siglip_debug_fill_workspace.argtypes = [vp, ctypes.c_uint16]
+        names += TEST_HOOKS
+    for name in names:
         getattr(lib, name).restype = getattr(lib, name).restype or ctypes.c_int
-    _lib = lib
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _hooks():
+    lib = load_library()
+    if not hasattr(lib, "siglip_debug_capture"):
+        raise RuntimeError("stage capture and workspace poisoning are test hooks: call "
+                           "use_test_hooks() before the library is first loaded")
     return lib
 
 
@@ -153,18 +185,20 @@ class Model:
         elif (out.dtype != torch.float16 or not out.is_contiguous()
               or tuple(out.shape) != (b, 1, self.width)):
             raise ValueError("out must be a contiguous float16 [B, 1, width] tensor")
+        elif out.device != pixels.device:
+            raise ValueError(f"out is on {out.device}, pixels on {pixels.device}: both must be on the same GPU")
         _check(load_library().siglip_encode(self.handle, pixels.data_ptr(), b, out.data_ptr(),
                                             _stream_ptr(stream)))
         return out
 
     # ---- diagnostics
     def debug_capture(self, layer: int) -> None:
-        _check(load_library().siglip_debug_capture(self.handle, layer))
+        _check(_hooks().siglip_debug_capture(self.handle, layer))
 
     def debug_stage_info(self, stage):
         s = STAGE[stage] if isinstance(stage, str) else stage
         r, c, l, e = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
-        _check(load_library().siglip_debug_stage_info(self.handle, s, ctypes.byref(r), ctypes.byref(c),
+        _check(_hooks().siglip_debug_stage_info(self.handle, s, ctypes.byref(r), ctypes.byref(c),
                                                       ctypes.byref(l), ctypes.byref(e)))
         return r.value, c.value, l.value, e.value
 
@@ -175,12 +209,12 @@ class Model:
         s = STAGE[stage] if isinstance(stage, str) else stage
         rows, cols, ld, eb = self.debug_stage_info(s)
         buf = np.empty(rows * ld * eb, np.uint8)
-        _check(load_library().siglip_debug_stage(self.handle, s, buf.ctypes.data, buf.nbytes))
+        _check(_hooks().siglip_debug_stage(self.handle, s, buf.ctypes.data, buf.nbytes))
         arr = buf.view(np.float16 if eb == 2 else np.uint8).reshape(rows, ld)
         return arr if full else arr[:, :cols]
 
     def debug_fill_workspace(self, pattern: int) -> None:
-        _check(load_library().siglip_debug_fill_workspace(self.handle, pattern))
+        _check(_hooks().siglip_debug_fill_workspace(self.handle, pattern))
 
     def debug_timing(self, classes) -> None:
         """Per-launch HIP-event timing of later encode calls for the given
@@ -221,11 +255,20 @@ class Model:
         self.close()
 
 
+def _span_ok(x, elems: int) -> bool:
+    """x's storage holds `elems` elements of its dtype from x.data_ptr() on."""
+    st = x.untyped_storage()
+    avail = st.nbytes() - (x.data_ptr() - st.data_ptr())
+    return elems * x.element_size() <= avail
+
+
 def attention(q, k, v, heads: int, head_dim: int, scale: float, out=None, row_stride: Optional[int] = None,
               tokens: Optional[int] = None, batch: Optional[int] = None, stream=None):
     """siglip_attention on CUDA float16 tensors or views; q/k/v rows hold
     heads*head_dim values at row_stride elements apart (default
-    heads*head_dim). batch and tokens default to q.shape[0] and q.shape[1]."""
+    heads*head_dim). batch and tokens default to q.shape[0] and q.shape[1].
+    Raises ValueError, before any launch, if a tensor is not on q's GPU or
+    its storage does not cover the rows the call reads or writes."""
     import torch
     b = batch if batch is not None else q.shape[0]
     t = tokens if tokens is not None else q.shape[1]
@@ -237,18 +280,17 @@ def attention(q, k, v, heads: int, head_dim: int, scale: float, out=None, row_st
     for x in (q, k, v, out):
         if x.device.type != "cuda" or x.dtype != torch.float16:
             raise ValueError("q, k, v, out must be CUDA float16")
+        if x.device != q.device:
+            raise ValueError("q, k, v and out must be on the same GPU")
+    if b < 1 or t < 1 or row_stride < w:
+        raise ValueError("batch, tokens >= 1 and row_stride >= heads*head_dim required")
+    span = (b * t - 1) * row_stride + w
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        if not _span_ok(x, span):
+            raise ValueError(f"{name}: its storage does not hold the {span} elements the call reads")
+    if not out.is_contiguous() or out.numel() < b * t * w or not _span_ok(out, b * t * w):
+        raise ValueError("out must be a contiguous tensor of at least batch*tokens*heads*head_dim elements")
     _check(load_library().siglip_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_stride,
                                            out.data_ptr(), b, heads, t, head_dim, float(scale),
                                            _stream_ptr(stream)))
     return out
-
-
-def e4m3_decode(codes: np.ndarray, scale_exp: int = -4) -> np.ndarray:
-    """Values of e4m3fn codes stored at scale 2^-scale_exp (test/diagnostic helper)."""
-    c = codes.astype(np.int32)
-    s = np.where(c & 0x80, -1.0, 1.0)
-    e = (c >> 3) & 0xF
-    m = (c & 7).astype(np.float64)
-    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
-    v = np.where((e == 0xF) & (m == 7), np.nan, v)
-    return s * v * 2.0 ** scale_exp

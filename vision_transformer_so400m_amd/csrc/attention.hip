@@ -607,9 +607,10 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
 //
 // V^T stage: 80 rows of 64 key bytes, 16-byte chunks swizzled by
 // (row >> 2) & 3 (16 consecutive rows read one chunk without bank conflicts).
-// Rows D..79 are read from the rows that follow the head's D rows in memory
-// (the next head's, or the buffer's slack after the last); they reach only
-// rows D..79 of O^T, which are never read. Row 80 holds e4m3(2^-exp), so the
+// The transfers fill whole 16-row groups, so rows D..79 are copies of the
+// head's row D-1 (the source row is clamped: nothing outside the head's D
+// rows is read); they reach only rows D..79 of O^T, which are never read.
+// Row 80 holds e4m3(2^-exp), so the
 // same MFMA yields each query's sum of its quantized probabilities (the scales
 // 2^4 and 2^-exp cancel in the division); rows 81..95 are zero.
 //
@@ -726,8 +727,10 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
       }
       ksrc[j] = kb8 + (img + kkey[j]) * krow + kcol + KCH_BYTES * kdc[j];
     } else if (jg < NDMA) {
+      // LDS row vr takes logical chunk vswz8(vr, lane & 3) of V^T row vr;
+      // rows D..79 take row D-1 instead, so nothing past the head is read
       const int vr = 16 * (jg - NK) + (lane >> 2);
-      vsrc[j] = vth + (int64_t)vr * vt_ld + 16 * vswz8(vr, lane & 3);
+      vsrc[j] = vth + (int64_t)min(vr, D - 1) * vt_ld + 16 * vswz8(vr, lane & 3);
     }
   }
   auto issue = [&](int kb) {

@@ -150,9 +150,8 @@ hipError_t launch_flash_attention_vt(const void* q, const void* k, int64_t ld, i
 
 // The same with the PV product in e4m3: vt holds codes of v * v_scale (bytes,
 // row stride vt_ld, a multiple of 16, zero codes in columns tokens..vt_ld-1;
-// the 80 - head_dim rows after the last head's must be readable), the
-// probabilities are quantized to e4m3(p * 2^4) in registers. v_scale is a
-// power of two in (0, 256].
+// only each head's head_dim rows are read), the probabilities are quantized
+// to e4m3(p * 2^4) in registers. v_scale is a power of two in (0, 256].
 hipError_t launch_flash_attention_vt8(const void* q, const void* k, int64_t ld, int qk8_pitch, const uint8_t* vt,
                                       int64_t vt_ld, void* o, int64_t ldo, int batch, int heads, int tokens,
                                       int head_dim, float scale, bool out_fp8, float out_scale, float v_scale,
@@ -177,6 +176,14 @@ hipError_t launch_map_fold(const f16* z, int64_t ldz, const f16* u_hi, const f16
                            int head_dim, int width, float scale, bool out_fp8, float out_scale, void* o,
                            int64_t ldo, hipStream_t s, int phase);
 
+// Create-time constants of the folded MAP head from the F32 blob tensors on
+// the device: q = probe Wq + bq (F32, and F16 in q16), u_hi/u_lo [16, width]
+// as for launch_map_fold, wvt [width, width] = W_v transposed. wkv is the
+// fused [width, 2 width] K/V weight.
+hipError_t launch_map_fold_prepare(const float* probe, const float* wq, const float* bq, const float* wkv, int width,
+                                   int heads, int head_dim, float* q, f16* q16, f16* u_hi, f16* u_lo, float* wvt,
+                                   hipStream_t s);
+
 // ------------------------------------------------------------ conversion
 // F16 [rows, cols] (row stride ldx) -> [rows, cols_pad] F16 or e4m3 codes of
 // x*scale, columns cols..cols_pad-1 set to zero.
@@ -194,6 +201,14 @@ hipError_t launch_weight_transpose(const float* w, int K, int N, void* wt,
 hipError_t launch_f32_convert(const float* x, int rows, int cols, void* y,
                               int cols_pad, bool out_fp8, float scale,
                               hipStream_t s);
+
+// V [batch, tokens, width] F16 (row stride ld elements, a multiple of 8) ->
+// vt [batch * width, vt_ld]: row b * width + c holds column c of image b for
+// tokens 0..tokens-1 and zeros in columns tokens..vt_ld-1 (vt_ld a multiple
+// of 64). With width = heads * head_dim, row (b heads + h) head_dim + d is
+// the V^T row of launch_flash_attention_vt. 16-byte aligned v and vt.
+hipError_t launch_vt_transpose(const f16* v, int64_t ld, int batch, int tokens, int width, f16* vt, int64_t vt_ld,
+                               hipStream_t s);
 
 // Zero columns c0..c1-1 of every row of an F16 [rows, ld] matrix.
 hipError_t launch_zero_cols(f16* p, int64_t rows, int64_t ld, int c0, int c1, hipStream_t s);

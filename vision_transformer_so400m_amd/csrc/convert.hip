@@ -10,6 +10,9 @@
 //    K-contiguous, zero padding; staged through LDS so both the F32 reads and
 //    the narrow writes are coalesced.
 //  * f32_convert: create-time F32 rows -> padded F16/e4m3 rows (the probe).
+//  * vt_transpose: V [batch, tokens, width] -> V^T per image ([b width + c]
+//    rows of tokens, zero past the last token), the layout the streaming
+//    attention kernel reads, for attention calls that receive V row-major.
 //  * fill_u16: workspace poisoning for the padding tests.
 #include "common.h"
 
@@ -88,6 +91,36 @@ __global__ __launch_bounds__(256) void f32_convert_kernel(const float* __restric
   }
 }
 
+// 64 tokens x 64 columns per workgroup through LDS: 16-byte reads along V
+// rows, 16-byte writes along V^T rows. The LDS row pitch of 66 halfs (33
+// words) puts the 8 rows one column read touches in distinct banks.
+__global__ __launch_bounds__(256) void vt_transpose_kernel(const f16* __restrict__ v, int64_t ld, int T, int width,
+                                                           f16* __restrict__ vt, int64_t vt_ld) {
+  constexpr int P = 66;
+  __shared__ uint32_t tile[64 * P / 2];
+  f16* th = reinterpret_cast<f16*>(tile);
+  const int b = blockIdx.z, t0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, ch = i & 7;
+    const int tok = t0 + r, col = c0 + 8 * ch;
+    i32x4 x = {0, 0, 0, 0};
+    if (tok < T && col < width) x = *reinterpret_cast<const i32x4*>(v + ((int64_t)b * T + tok) * ld + col);
+    uint32_t* d = tile + (r * P + 8 * ch) / 2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d[e] = (uint32_t)x[e];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int cc = i >> 3, ch = i & 7;
+    const int col = c0 + cc;
+    if (col >= width) continue;
+    f16x8 y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = th[(8 * ch + e) * P + cc];
+    *reinterpret_cast<f16x8*>(vt + ((int64_t)b * width + col) * vt_ld + t0 + 8 * ch) = y;
+  }
+}
+
 __global__ __launch_bounds__(256) void zero_cols_kernel(f16* __restrict__ p, int64_t rows, int64_t ld, int c0, int w) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= rows * w) return;
@@ -142,6 +175,17 @@ hipError_t launch_f32_convert(const float* x, int rows, int cols, void* y, int c
     hipLaunchKernelGGL(f32_convert_kernel<true>, grid, dim3(256), 0, s, x, rows, cols, y, cols_pad, scale);
   else
     hipLaunchKernelGGL(f32_convert_kernel<false>, grid, dim3(256), 0, s, x, rows, cols, y, cols_pad, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_transpose(const f16* v, int64_t ld, int batch, int tokens, int width, f16* vt, int64_t vt_ld,
+                               hipStream_t s) {
+  auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (batch < 1 || batch > 65535 || tokens < 1 || width < 8 || (width & 7) || ld < width || (ld & 7) ||
+      vt_ld < tokens || (vt_ld & 63) || !a16(v) || !a16(vt))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((width + 63) / 64), (unsigned)(vt_ld / 64), (unsigned)batch);
+  hipLaunchKernelGGL(vt_transpose_kernel, grid, dim3(256), 0, s, v, ld, tokens, width, vt, vt_ld);
   return hipGetLastError();
 }
 

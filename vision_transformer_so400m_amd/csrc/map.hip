@@ -284,6 +284,58 @@ __global__ __launch_bounds__(1024) void map_vproj_kernel(const float* __restrict
   }
 }
 
+// ---- create-time constants of the fold (one launch each, F32 arithmetic).
+// q[n] = bq[n] + sum_k probe[k] Wq[k][n]; also kept as F16 for inspection.
+__global__ __launch_bounds__(256) void map_query_kernel(const float* __restrict__ probe, const float* __restrict__ wq,
+                                                        const float* __restrict__ bq, int width, float* __restrict__ q,
+                                                        f16* __restrict__ q16) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= width) return;
+  float acc = bq[n];
+  for (int k = 0; k < width; ++k) acc = fmaf(probe[k], wq[(int64_t)k * width + n], acc);
+  q[n] = acc;
+  q16[n] = (f16)acc;
+}
+
+// u_h[k] = sum_d W_k[k][h D + d] q[h D + d] for head slots h < heads (slots
+// up to kMapHeads are zero), split into F16 parts hi = f16(u), lo = f16(u - hi).
+// W_k is the first width columns of the fused [width, 2 width] K/V weight.
+__global__ __launch_bounds__(256) void map_u_kernel(const float* __restrict__ wkv, const float* __restrict__ q,
+                                                    int width, int heads, int head_dim, f16* __restrict__ u_hi,
+                                                    f16* __restrict__ u_lo) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= kMapHeads * width) return;
+  const int h = i / width, k = i - h * width;
+  float u = 0.f;
+  if (h < heads) {
+    const float* wr = wkv + (int64_t)k * 2 * width + h * head_dim;
+    const float* qh = q + h * head_dim;
+    for (int d = 0; d < head_dim; ++d) u = fmaf(wr[d], qh[d], u);
+  }
+  const f16 hi = (f16)u;
+  u_hi[i] = hi;
+  u_lo[i] = (f16)(u - (float)hi);
+}
+
+// wvt[n][k] = W_v[k][n] = wkv[k][width + n] (32 x 32 tiles through LDS)
+__global__ __launch_bounds__(256) void map_wv_transpose_kernel(const float* __restrict__ wkv, int width,
+                                                               float* __restrict__ wvt) {
+  __shared__ float tile[32][33];
+  const int k0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+#pragma unroll
+  for (int j = 0; j < 32; j += 8) {
+    const int k = k0 + ty + j, n = n0 + tx;
+    tile[ty + j][tx] = (k < width && n < width) ? wkv[(int64_t)k * 2 * width + width + n] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 32; j += 8) {
+    const int n = n0 + ty + j, k = k0 + tx;
+    if (n < width && k < width) wvt[(int64_t)n * width + k] = tile[tx][ty + j];
+  }
+}
+
 }  // namespace
 
 bool map_fold_supported(int width, int heads, int head_dim, int tokens) {
@@ -321,6 +373,24 @@ hipError_t launch_map_fold(const f16* z, int64_t ldz, const f16* u_hi, const f16
   else
     hipLaunchKernelGGL(map_vproj_kernel<false>, grid, block, lds, s, zbar, wvt, bv, width, head_dim, batch, o, ldo,
                        out_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_map_fold_prepare(const float* probe, const float* wq, const float* bq, const float* wkv, int width,
+                                   int heads, int head_dim, float* q, f16* q16, f16* u_hi, f16* u_lo, float* wvt,
+                                   hipStream_t s) {
+  if (width < 1 || width > 4096 || heads < 1 || heads > kMapHeads || head_dim < 1 || heads * head_dim != width)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(map_query_kernel, dim3((unsigned)((width + 255) / 256)), dim3(256), 0, s, probe, wq, bq, width, q,
+                     q16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(map_u_kernel, dim3((unsigned)((kMapHeads * width + 255) / 256)), dim3(256), 0, s, wkv, q, width,
+                     heads, head_dim, u_hi, u_lo);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((width + 31) / 32), (unsigned)((width + 31) / 32));
+  hipLaunchKernelGGL(map_wv_transpose_kernel, grid, dim3(256), 0, s, wkv, width, wvt);
   return hipGetLastError();
 }
 

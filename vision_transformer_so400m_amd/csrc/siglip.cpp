@@ -6,29 +6,37 @@
 //   X [B*T, 588] --pad/convert--> Xp [B*T, 640]
 //   H = Xp Wpe + bpe + pos[t]                      (GEMM, EPI_BIAS_POS)
 //   per layer:  A = LN1(H)                         (layernorm)
-//               QKV = A Wqkv + b                   (GEMM, EPI_BIAS)
-//               O = attention(QKV views)           (flash attention)
+//               QKV = A Wqkv + b                   (GEMM, EPI_QKV: V transposed)
+//               O = attention(Q, K, V^T)           (streaming flash attention)
 //               H = O Wo + bo + H                  (GEMM, EPI_BIAS_RES, in place)
 //               A = LN2(H)
 //               U = gelu(A W1 + b1)                (GEMM, EPI_BIAS_GELU)
 //               H = U W2 + b2 + H                  (GEMM, EPI_BIAS_RES)
-//   Z = LN(H); KV = Z Wkv + bkv; o = probe-attention(q, KV)
+//   Z = LN(H); o = probe attention of q over K = Z Wk + bk, V = Z Wv + bv
 //   y = o Wo' + bo'; out = gelu(LN(y) W1' + b1') W2' + b2' + y
 //
-// The probe query q = probe Wq + bq is image-independent ("Each batch uses the
-// same learned probe") and is computed once at create time by the same GEMM.
+// The probe is the same for every image (same page, intro: one learned probe
+// shared by the whole batch), so its query q = probe Wq + bq is a model
+// constant. By default the MAP K/V projection is folded away: create computes
+// q, u_h = W_k,h q_h and W_v transposed with small GPU kernels, and each call
+// computes the scores Z u_h and (sum_t p_t Z_t) W_v,h + b_v,h (map.hip). With
+// the explicit K/V option, q comes from the projection GEMM at create and
+// every call runs the K/V GEMM and the probe attention.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <climits>
 #include <exception>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
 
 #include "../../include/siglip.h"
+#include "../../include/siglip_test_hooks.h"
 #include "common.h"
 
 using namespace siglip;
@@ -242,48 +250,38 @@ Gemm make_gemm_block(siglip_model* m, const TensorRef& w, const TensorRef& b, in
   return make_gemm(m, ws, bs, staging);
 }
 
-// Constants of the folded MAP head, on the host in float64: q = probe Wq + bq
-// (also kept as F16 for the MAP_Q diagnostic), u_h = W_k,h q_h stored as
-// F16 hi + lo parts in 16 head rows, W_v (transposed per head) and b_v F32.
+// Constants of the folded MAP head, computed on the device from the F32 blob
+// tensors (map.hip, launch_map_fold_prepare): q = probe Wq + bq (kept as F16
+// for the MAP_Q checkpoint), u_h = W_k,h q_h as F16 hi + lo parts in 16 head
+// rows, W_v transposed per head; b_v is the V half of the fused bias.
 void make_map_fold(siglip_model* m, const TensorRef& probe, const TensorRef& qw, const TensorRef& qb,
                    const TensorRef& kvw, const TensorRef& kvb) {
-  const int W = m->width, H = m->heads, D = m->head_dim;
-  std::vector<double> q(W);
-  for (int n = 0; n < W; ++n) q[n] = qb.host[n];
-  for (int k = 0; k < W; ++k) {
-    const double p = probe.host[k];
-    const float* wr = qw.host + (int64_t)k * W;
-    for (int n = 0; n < W; ++n) q[n] += p * wr[n];
-  }
-  std::vector<f16> qh(W), uh((size_t)16 * W, (f16)0.0f), ul((size_t)16 * W, (f16)0.0f);
-  for (int n = 0; n < W; ++n) qh[n] = (f16)q[n];
-  for (int k = 0; k < W; ++k) {
-    const float* wr = kvw.host + (int64_t)k * 2 * W;  // K block: columns 0 .. W-1
-    for (int h = 0; h < H; ++h) {
-      double u = 0.0;
-      for (int d = 0; d < D; ++d) u += (double)wr[h * D + d] * q[h * D + d];
-      const f16 hi = (f16)u;
-      uh[(size_t)h * W + k] = hi;
-      ul[(size_t)h * W + k] = (f16)(u - (double)hi);
-    }
-  }
-  // W_v transposed per head: wvt[(h*D + d) * W + k] = W_v[k][h*D + d]
-  std::vector<float> wv((size_t)W * W), bv(W);
-  for (int k = 0; k < W; ++k) {
-    const float* vr = kvw.host + (int64_t)k * 2 * W + W;
-    for (int n = 0; n < W; ++n) wv[(size_t)n * W + k] = vr[n];
-  }
-  std::memcpy(bv.data(), kvb.host + W, (size_t)W * 4);
+  const int W = m->width;
   m->map_q = static_cast<f16*>(m->dalloc((size_t)W * 2));
-  m->u_hi = static_cast<f16*>(m->dalloc(uh.size() * 2));
-  m->u_lo = static_cast<f16*>(m->dalloc(ul.size() * 2));
-  m->wv = static_cast<float*>(m->dalloc(wv.size() * 4));
-  m->bv = static_cast<float*>(m->dalloc(bv.size() * 4));
-  hip_check(hipMemcpy(m->map_q, qh.data(), qh.size() * 2, hipMemcpyHostToDevice), "hipMemcpy");
-  hip_check(hipMemcpy(m->u_hi, uh.data(), uh.size() * 2, hipMemcpyHostToDevice), "hipMemcpy");
-  hip_check(hipMemcpy(m->u_lo, ul.data(), ul.size() * 2, hipMemcpyHostToDevice), "hipMemcpy");
-  hip_check(hipMemcpy(m->wv, wv.data(), wv.size() * 4, hipMemcpyHostToDevice), "hipMemcpy");
-  hip_check(hipMemcpy(m->bv, bv.data(), bv.size() * 4, hipMemcpyHostToDevice), "hipMemcpy");
+  m->u_hi = static_cast<f16*>(m->dalloc((size_t)16 * W * 2));
+  m->u_lo = static_cast<f16*>(m->dalloc((size_t)16 * W * 2));
+  m->wv = static_cast<float*>(m->dalloc((size_t)W * W * 4));
+  m->bv = static_cast<float*>(m->dalloc((size_t)W * 4));
+  hip_check(hipMemcpy(m->bv, kvb.host + W, (size_t)W * 4, hipMemcpyHostToDevice), "hipMemcpy");
+  // the blob tensors the constants come from, for the duration of the call
+  float* tmp = nullptr;
+  const size_t nf = (size_t)W + (size_t)W * W + W + (size_t)W * 2 * W + W;  // probe, Wq, bq, Wkv, q
+  hip_check(hipMalloc(&tmp, nf * 4), "hipMalloc");
+  float* d_probe = tmp;
+  float* d_wq = d_probe + W;
+  float* d_bq = d_wq + (size_t)W * W;
+  float* d_wkv = d_bq + W;
+  float* d_q = d_wkv + (size_t)W * 2 * W;
+  hipError_t e = hipMemcpy(d_probe, probe.host, (size_t)W * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(d_wq, qw.host, (size_t)W * W * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(d_bq, qb.host, (size_t)W * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(d_wkv, kvw.host, (size_t)W * 2 * W * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = launch_map_fold_prepare(d_probe, d_wq, d_bq, d_wkv, W, m->heads, m->head_dim, d_q, m->map_q, m->u_hi,
+                                m->u_lo, m->wv, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  (void)hipFree(tmp);
+  hip_check(e, "MAP fold constants");
 }
 
 // The activation buffers of the images [b0, ...) of a call: every buffer is
@@ -886,10 +884,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
         {&m->xp, M * m->patch_pad * es}, {(void**)&m->h, M * W * 2}, {&m->a, M * W * es},
         {(void**)&m->qkv, M * 3 * W * 2}, {&m->o, M * W * es}, {&m->u, M * m->mlp_pad * es},
         {&m->mo, B * W * es}, {(void**)&m->my, B * W * 2}, {&m->ma, B * W * es}, {&m->mu, B * m->mlp_pad * es},
-        // V^T at F16 size in both modes: with e4m3 codes the unused half is the
-        // slack that the e4m3 attention kernel's reads of rows D..79 past the
-        // last head land in
-        {(void**)&m->vt, m->vt_path ? B * W * m->tokens_pad * 2 : 0},
+        // V^T: F16, or e4m3 codes with the e4m3 PV product
+        {(void**)&m->vt, m->vt_path ? B * W * m->tokens_pad * (m->attn_fp8 ? 1 : 2) : 0},
         {(void**)&m->mscores, m->map_fold ? M * 16 * 4 : 0},
         {(void**)&m->zbar, m->map_fold ? B * 16 * W * 4 : 0},
     };
@@ -908,7 +904,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     hip_check(hipEventCreateWithFlags(&m->join_ev, hipEventDisableTiming), "hipEventCreate");
 
     // probe query, once: q = probe Wq + bq (same GEMM as every projection;
-    // the folded path computed it on the host with the fold constants)
+    // the folded path computed it with the fold constants)
     if (!m->map_fold) {
     void* probe_op = m->dalloc((size_t)m->mq.k_pad * es);
     hip_check(hipMemcpy(staging, probe.host, (size_t)W * 4, hipMemcpyHostToDevice), "hipMemcpy");
@@ -928,6 +924,82 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_OUT_OF_MEMORY, "host allocation failed");
   }
   *out = m;
+  return SIGLIP_OK;
+}
+
+// Library-owned V^T staging of siglip_attention, one buffer per device,
+// grown on demand (the call that needs more than any before it allocates)
+// and kept until the process ends.
+std::mutex g_vt_mu;
+constexpr int kMaxDevices = 64;
+void* g_vt_buf[kMaxDevices] = {};
+size_t g_vt_bytes[kMaxDevices] = {};
+
+int vt_staging(size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SIGLIP_E_UNSUPPORTED, "device ordinal above 63");
+  std::lock_guard<std::mutex> lock(g_vt_mu);
+  if (g_vt_bytes[dev] < need) {
+    if (g_vt_buf[dev]) (void)hipFree(g_vt_buf[dev]);
+    g_vt_buf[dev] = nullptr;
+    g_vt_bytes[dev] = 0;
+    e = hipMalloc(&g_vt_buf[dev], need);
+    if (e != hipSuccess) {
+      g_vt_buf[dev] = nullptr;
+      return fail(e == hipErrorOutOfMemory ? SIGLIP_E_OUT_OF_MEMORY : SIGLIP_E_HIP,
+                  std::string("V^T staging: ") + hipGetErrorString(e));
+    }
+    g_vt_bytes[dev] = need;
+  }
+  *out = g_vt_buf[dev];
+  return SIGLIP_OK;
+}
+
+// Standalone attention. Head widths the streaming kernel takes (64, 72, 80)
+// run the encoder's own kernel: V is first transposed per image into V^T
+// rows (zeros past the last token), in `scratch` when the caller supplies
+// one of scratch_bytes, else in the library's staging buffer. Other head
+// widths run the register-staged kernel, which needs no staging.
+int attention_impl(const void* q, const void* k, const void* v, int64_t ld, void* o, int32_t batch, int32_t heads,
+                   int32_t tokens, int32_t head_dim, float scale, void* hip_stream, void* scratch,
+                   size_t scratch_bytes) {
+  if (!q || !k || !v || !o) return fail(SIGLIP_E_INVALID_ARG, "null q, k, v or o");
+  if (batch < 1 || heads < 1 || tokens < 1 || batch > 65535 || heads > 65535)
+    return fail(SIGLIP_E_INVALID_ARG, "batch, heads and tokens must be >= 1 (batch, heads <= 65535)");
+  if (head_dim < 8 || head_dim > 80 || head_dim % 8)
+    return fail(SIGLIP_E_UNSUPPORTED, "head_dim must be a multiple of 8 in 8..80");
+  if (ld < (int64_t)heads * head_dim || ld % 8)
+    return fail(SIGLIP_E_INVALID_ARG, "row_stride_elems must be >= heads*head_dim and a multiple of 8");
+  for (const void* p : {q, k, v, (const void*)o})
+    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(SIGLIP_E_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(SIGLIP_E_INVALID_ARG, "scale must be finite and > 0");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t width = (int64_t)heads * head_dim;
+  if (width > INT32_MAX) return fail(SIGLIP_E_INVALID_ARG, "heads*head_dim too large");
+  hipError_t e;
+  if (flash_attention_vt_supported(head_dim)) {
+    const int64_t vt_ld = round_up(tokens, 64);
+    const size_t need = (size_t)batch * (size_t)width * (size_t)vt_ld * 2;
+    void* vt = scratch;
+    if (!vt) {
+      const int st = vt_staging(need, &vt);
+      if (st != SIGLIP_OK) return st;
+    } else if (need > scratch_bytes) {
+      return fail(SIGLIP_E_INVALID_ARG, "V^T staging needs " + std::to_string(need) + " bytes, scratch holds " +
+                                            std::to_string(scratch_bytes));
+    }
+    e = launch_vt_transpose(static_cast<const f16*>(v), ld, batch, tokens, (int)width, static_cast<f16*>(vt), vt_ld,
+                            s);
+    if (e == hipSuccess)
+      e = launch_flash_attention_vt(q, k, ld, 0, static_cast<const f16*>(vt), vt_ld, o, width, batch, heads, tokens,
+                                    head_dim, scale, false, 1.0f, s);
+  } else {
+    e = launch_flash_attention(static_cast<const f16*>(q), static_cast<const f16*>(k), static_cast<const f16*>(v), ld,
+                               o, width, batch, heads, tokens, head_dim, scale, false, 1.0f, s);
+  }
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   return SIGLIP_OK;
 }
 
@@ -967,22 +1039,7 @@ SIGLIP_API int siglip_encode(siglip_model* m, const void* pixels_f16, int32_t ba
 SIGLIP_API int siglip_attention(const void* q, const void* k, const void* v, int64_t row_stride_elems, void* o,
                                 int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim, float scale,
                                 void* hip_stream) {
-  if (!q || !k || !v || !o) return fail(SIGLIP_E_INVALID_ARG, "null q, k, v or o");
-  if (batch < 1 || heads < 1 || tokens < 1 || batch > 65535 || heads > 65535)
-    return fail(SIGLIP_E_INVALID_ARG, "batch, heads and tokens must be >= 1 (batch, heads <= 65535)");
-  if (head_dim < 8 || head_dim > 80 || head_dim % 8)
-    return fail(SIGLIP_E_UNSUPPORTED, "head_dim must be a multiple of 8 in 8..80");
-  if (row_stride_elems < (int64_t)heads * head_dim || row_stride_elems % 8)
-    return fail(SIGLIP_E_INVALID_ARG, "row_stride_elems must be >= heads*head_dim and a multiple of 8");
-  for (const void* p : {q, k, v, (const void*)o})
-    if (reinterpret_cast<uintptr_t>(p) & 15) return fail(SIGLIP_E_INVALID_ARG, "pointers must be 16-byte aligned");
-  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(SIGLIP_E_INVALID_ARG, "scale must be finite and > 0");
-  hipError_t e = launch_flash_attention(static_cast<const f16*>(q), static_cast<const f16*>(k),
-                                        static_cast<const f16*>(v), row_stride_elems, o, (int64_t)heads * head_dim,
-                                        batch, heads, tokens, head_dim, scale, false, 1.0f,
-                                        static_cast<hipStream_t>(hip_stream));
-  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("attention launch: ") + hipGetErrorString(e));
-  return SIGLIP_OK;
+  return attention_impl(q, k, v, row_stride_elems, o, batch, heads, tokens, head_dim, scale, hip_stream, nullptr, 0);
 }
 
 SIGLIP_API int siglip_destroy(siglip_model* m) {
@@ -1022,6 +1079,7 @@ SIGLIP_API int siglip_model_info(const siglip_model* m, int32_t* width, int32_t*
   return SIGLIP_OK;
 }
 
+#ifdef SIGLIP_TEST_HOOKS
 SIGLIP_API int siglip_debug_capture(siglip_model* m, int32_t layer) {
   if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
   if (layer >= m->layers) return fail(SIGLIP_E_INVALID_ARG, "capture layer beyond the model's layers");
@@ -1071,6 +1129,8 @@ SIGLIP_API int siglip_debug_stage(const siglip_model* m, int32_t stage, void* ds
   return SIGLIP_OK;
 }
 
+#endif  // SIGLIP_TEST_HOOKS
+
 SIGLIP_API int siglip_debug_timing(siglip_model* m, uint32_t class_mask) {
   if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
   if (class_mask >> SIGLIP_K_COUNT) return fail(SIGLIP_E_INVALID_ARG, "class_mask selects unknown classes");
@@ -1102,6 +1162,7 @@ SIGLIP_API int siglip_debug_timing_read(siglip_model* m, int32_t kernel_class, d
   return SIGLIP_OK;
 }
 
+#ifdef SIGLIP_TEST_HOOKS
 SIGLIP_API int siglip_debug_fill_workspace(siglip_model* m, uint16_t pattern) {
   if (!m) return fail(SIGLIP_E_INVALID_ARG, "null model");
   hipError_t e = launch_fill_u16(m->ws, m->ws_bytes / 2, pattern, nullptr);
@@ -1109,5 +1170,6 @@ SIGLIP_API int siglip_debug_fill_workspace(siglip_model* m, uint16_t pattern) {
   if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("fill: ") + hipGetErrorString(e));
   return SIGLIP_OK;
 }
+#endif  // SIGLIP_TEST_HOOKS
 
 }  // extern "C"
