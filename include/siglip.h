@@ -185,6 +185,28 @@ SIGLIP_API int siglip_attention(const void* q, const void* k, const void* v,
                                 int32_t batch, int32_t heads, int32_t tokens,
                                 int32_t head_dim, float scale, void* hip_stream);
 
+/*
+ * siglip_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, the same kernels and the same results,
+ * but the V^T staging lives in a fixed 64 MiB device array of the library
+ * (a file-scope __device__ array, one per GPU, held until the process
+ * ends) instead of a buffer it allocates. The call makes no hipMalloc,
+ * hipFree or other allocating call; the first call on a device looks up
+ * the array's device address (hipGetSymbolAddress) once.
+ * Limit: batch * heads*head_dim * round_up(tokens, 64) * 2 <= 64 MiB for
+ * head widths 64, 72 and 80 (the attention workload [32, 729, 16 x 72]
+ * needs 56.6 MB); larger calls fail with INVALID_ARG before any launch.
+ * Every call on a GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap in time on one GPU (different streams, no
+ * ordering) race. Each call writes every staging byte it reads (V^T and its
+ * zero padding) before reading it. Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+SIGLIP_API int siglip_attention_noalloc(const void* q, const void* k, const void* v,
+                                        int64_t row_stride_elems, void* o,
+                                        int32_t batch, int32_t heads, int32_t tokens,
+                                        int32_t head_dim, float scale, void* hip_stream);
+
 /* Free the model's device memory. Synchronises the device first. NULL is a
  * no-op returning SIGLIP_OK. */
 SIGLIP_API int siglip_destroy(siglip_model* m);

@@ -27,7 +27,7 @@ STAGES = ["EMBED", "LN1", "QKV", "ATTN", "H_ATTN", "LN2", "MLP_HIDDEN", "H_OUT",
           "FINAL_LN", "MAP_KV", "MAP_ATTN", "MAP_Y", "MAP_LN", "MAP_HIDDEN", "MAP_Q", "V_T"]
 STAGE = {n: i for i, n in enumerate(STAGES)}
 
-EXPORTED = ["siglip_create", "siglip_encode", "siglip_attention", "siglip_destroy",
+EXPORTED = ["siglip_create", "siglip_encode", "siglip_attention", "siglip_attention_noalloc", "siglip_destroy",
             "siglip_status_string", "siglip_last_error", "siglip_model_info",
             "siglip_debug_timing", "siglip_debug_timing_read"]
 TEST_HOOKS = ["siglip_debug_capture", "siglip_debug_stage_info", "siglip_debug_stage",
@@ -87,6 +87,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.siglip_create.argtypes = [vp, ctypes.c_size_t, P(siglip_options), P(vp)]
     lib.siglip_encode.argtypes = [vp, vp, i32, vp, vp]
     lib.siglip_attention.argtypes = [vp, vp, vp, i64, vp, i32, i32, i32, i32, ctypes.c_float, vp]
+    lib.siglip_attention_noalloc.argtypes = [vp, vp, vp, i64, vp, i32, i32, i32, i32, ctypes.c_float, vp]
     lib.siglip_destroy.argtypes = [vp]
     lib.siglip_status_string.argtypes = [ctypes.c_int]
     lib.siglip_status_string.restype = ctypes.c_char_p
@@ -263,12 +264,15 @@ def _span_ok(x, elems: int) -> bool:
 
 
 def attention(q, k, v, heads: int, head_dim: int, scale: float, out=None, row_stride: Optional[int] = None,
-              tokens: Optional[int] = None, batch: Optional[int] = None, stream=None):
+              tokens: Optional[int] = None, batch: Optional[int] = None, stream=None, noalloc: bool = False):
     """siglip_attention on CUDA float16 tensors or views; q/k/v rows hold
     heads*head_dim values at row_stride elements apart (default
     heads*head_dim). batch and tokens default to q.shape[0] and q.shape[1].
-    Raises ValueError, before any launch, if a tensor is not on q's GPU or
-    its storage does not cover the rows the call reads or writes."""
+    noalloc=True calls siglip_attention_noalloc (the library's fixed scratch
+    array instead of its allocated staging buffer; out must be given, so
+    nothing is allocated). Raises ValueError, before any launch, if a tensor
+    is not on q's GPU or its storage does not cover the rows the call reads
+    or writes."""
     import torch
     b = batch if batch is not None else q.shape[0]
     t = tokens if tokens is not None else q.shape[1]
@@ -276,6 +280,8 @@ def attention(q, k, v, heads: int, head_dim: int, scale: float, out=None, row_st
     if row_stride is None:
         row_stride = w
     if out is None:
+        if noalloc:
+            raise ValueError("noalloc=True needs out")
         out = torch.empty((b, t, w), dtype=torch.float16, device=q.device)
     for x in (q, k, v, out):
         if x.device.type != "cuda" or x.dtype != torch.float16:
@@ -290,7 +296,8 @@ def attention(q, k, v, heads: int, head_dim: int, scale: float, out=None, row_st
             raise ValueError(f"{name}: its storage does not hold the {span} elements the call reads")
     if not out.is_contiguous() or out.numel() < b * t * w or not _span_ok(out, b * t * w):
         raise ValueError("out must be a contiguous tensor of at least batch*tokens*heads*head_dim elements")
-    _check(load_library().siglip_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_stride,
-                                           out.data_ptr(), b, heads, t, head_dim, float(scale),
-                                           _stream_ptr(stream)))
+    lib = load_library()
+    fn = lib.siglip_attention_noalloc if noalloc else lib.siglip_attention
+    _check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), row_stride, out.data_ptr(), b, heads, t, head_dim,
+              float(scale), _stream_ptr(stream)))
     return out

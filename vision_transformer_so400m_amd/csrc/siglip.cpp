@@ -957,6 +957,36 @@ int vt_staging(size_t need, void** out) {
   return SIGLIP_OK;
 }
 
+// Scratch of siglip_attention_noalloc: a fixed device array, so that entry
+// point allocates nothing. Every GPU the library runs on holds its own copy
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: host code uses only the per-device address that
+// hipGetSymbolAddress returns (static_scratch below).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SIGLIP_E_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SIGLIP_E_UNSUPPORTED, "device ordinal above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SIGLIP_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SIGLIP_OK;
+}
+
 // Standalone attention. Head widths the streaming kernel takes (64, 72, 80)
 // run the encoder's own kernel: V is first transposed per image into V^T
 // rows (zeros past the last token), in `scratch` when the caller supplies
@@ -1040,6 +1070,29 @@ SIGLIP_API int siglip_attention(const void* q, const void* k, const void* v, int
                                 int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim, float scale,
                                 void* hip_stream) {
   return attention_impl(q, k, v, row_stride_elems, o, batch, heads, tokens, head_dim, scale, hip_stream, nullptr, 0);
+}
+
+SIGLIP_API int siglip_attention_noalloc(const void* q, const void* k, const void* v, int64_t row_stride_elems,
+                                        void* o, int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim,
+                                        float scale, void* hip_stream) {
+  // the same argument checks as siglip_attention come first, so a bad call
+  // fails before the scratch is looked up
+  if (!q || !k || !v || !o) return fail(SIGLIP_E_INVALID_ARG, "null q, k, v or o");
+  if (batch < 1 || heads < 1 || tokens < 1 || batch > 65535 || heads > 65535)
+    return fail(SIGLIP_E_INVALID_ARG, "batch, heads and tokens must be >= 1 (batch, heads <= 65535)");
+  if (head_dim < 8 || head_dim > 80 || head_dim % 8)
+    return fail(SIGLIP_E_UNSUPPORTED, "head_dim must be a multiple of 8 in 8..80");
+  if (flash_attention_vt_supported(head_dim)) {
+    const size_t need = (size_t)batch * (size_t)heads * head_dim * (size_t)round_up(tokens, 64) * 2;
+    if (need > kStaticScratchBytes)
+      return fail(SIGLIP_E_INVALID_ARG, "batch*heads*head_dim*round_up(tokens,64)*2 = " + std::to_string(need) +
+                                            " bytes exceeds the 64 MiB static scratch of siglip_attention_noalloc");
+  }
+  void* p = nullptr;
+  const int st = static_scratch(&p);
+  if (st != SIGLIP_OK) return st;
+  return attention_impl(q, k, v, row_stride_elems, o, batch, heads, tokens, head_dim, scale, hip_stream, p,
+                        kStaticScratchBytes);
 }
 
 SIGLIP_API int siglip_destroy(siglip_model* m) {
