@@ -15,7 +15,8 @@
 // operand scale is folded into acc_scale). F32 accumulation.
 //
 // Tiling: a workgroup of 4 or 8 waves owns a BM x BN output tile and walks K in
-// 128-byte slices (64 F16 or 128 e4m3 values per row). Slices go global ->
+// 128-byte slices (64 F16 or 128 e4m3 values per row; 64-byte slices for the
+// MLP-up tile). Slices go global ->
 // LDS directly (global_load_lds_dwordx4) into a ring of STAGES buffers, so the
 // loads of the next slices are in flight while one is multiplied. LDS rows are
 // 128 bytes with the 16-byte chunk index XOR-swizzled (swz below), so the 16
@@ -32,29 +33,40 @@
 namespace siglip {
 namespace {
 
-constexpr int kRowBytes = 128;  // K bytes of one LDS tile row
+constexpr int kRowBytes = 128;  // K bytes of one LDS tile row (the default K slice)
 
-template <int BM, int BN, int WM, int WN>
+// RB: K bytes of one LDS tile row (one K slice): 128, or 64 for tiles that
+// need a deeper ring in less LDS.
+template <int BM, int BN, int WM, int WN, int RB = kRowBytes>
 struct Tile {
   static constexpr int WAVES_N = BN / WN;
   static constexpr int WAVES_M = BM / WM;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
+  static_assert(RB == 64 || RB == 128, "64- or 128-byte K slices");
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int TM = WM / 32;
   static constexpr int TN = WN / 32;
-  static constexpr int ROWS_PER_ROUND = 8 * WAVES;  // tile rows one DMA round fills
+  static constexpr int RPW = 1024 / RB;             // tile rows one wave's 1 KiB transfer fills
+  static constexpr int ROWS_PER_ROUND = RPW * WAVES;  // tile rows one DMA round fills
   static_assert(BM % ROWS_PER_ROUND == 0 && BN % ROWS_PER_ROUND == 0, "whole DMA rounds");
-  static constexpr int STAGE = (BM + BN) * kRowBytes;
+  static constexpr int STAGE = (BM + BN) * RB;
 };
 
-// 16-byte chunk swizzle of a 128-byte LDS row. A fragment read has 16 lanes
-// reading one logical chunk of 16 consecutive rows; with 64 banks of 4 bytes
-// two 128-byte rows span all banks, so (row & 1) picks the half and the chunk
-// must differ across the 8 rows of each parity: chunk ^ (row & 7) ^ ((row >> 3)
-// & 1) does that (and is also a bijection on any 8 aligned rows).
-__device__ __forceinline__ int swz_key(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key(row); }
+// 16-byte chunk swizzle of an LDS row. A fragment read has 16 lanes reading
+// one logical chunk of 16 consecutive rows; 64 banks of 4 bytes span 256
+// bytes. 128-byte rows: two rows span all banks, so (row & 1) picks the half
+// and the chunk must differ across the 8 rows of each parity: chunk ^ (row &
+// 7) ^ ((row >> 3) & 1). 64-byte rows: four rows span all banks, so the chunk
+// must differ across rows r, r+4, r+8, r+12: chunk ^ ((row >> 2) & 3). Both
+// are bijections on the chunks of any row.
+template <int RB = kRowBytes>
+__device__ __forceinline__ int swz_key(int row) {
+  if constexpr (RB == 128) return (row & 7) ^ ((row >> 3) & 1);
+  else return (row >> 2) & 3;
+}
+template <int RB = kRowBytes>
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ swz_key<RB>(row); }
 
 // Element type of the output tile staged in LDS: F32 while a residual is
 // still to be added (one rounding), else the output type (for EPI_QKV the Q
@@ -105,9 +117,12 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8>
-__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmArgs g) {
-  using T = Tile<BM, BN, WM, WN>;
+// MINW: workgroups per CU the register allocation must allow (2 for the tile
+// that relies on two workgroups sharing a CU).
+template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8, int RB = kRowBytes,
+          int MINW = 1>
+__global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(GemmArgs g) {
+  using T = Tile<BM, BN, WM, WN, RB>;
   static_assert(STAGES >= 2, "at least double buffering");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * T::STAGE];
 
@@ -123,22 +138,23 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
   tile_of(blockIdx.x, ntm, ntn, g.group_m, &tm, &tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
-  const int nk = (g.K * E) / kRowBytes;
+  const int nk = (g.K * E) / RB;
 
   // ---- global -> LDS transfer assignment. A stage holds BM rows of A then
-  // BN rows of Wt, 128 bytes each, chunk-swizzled. Transfer j of wave w
-  // fills tile rows R j + 8 w .. +7 (R = 8 x waves); lane i lands at row
-  // R j + 8 w + i/8, physical chunk i%8, so it fetches logical chunk
-  // (i%8) ^ swz_key(row).
+  // BN rows of Wt, RB bytes each, chunk-swizzled. Transfer j of wave w fills
+  // tile rows R j + RPW w .. +RPW-1 (R = RPW x waves); lane i lands at row
+  // R j + RPW w + i / CPR, physical chunk i % CPR (CPR = RB / 16 chunks per
+  // row), so it fetches logical chunk swz(row, i % CPR). R j is a multiple of
+  // 16, so the swizzle key depends on RPW w + i / CPR only.
   constexpr int R = T::ROWS_PER_ROUND;
+  constexpr int CPR = RB / 16;
   constexpr int CH = (BM + BN) / R;  // transfers per thread per stage
-  const int rr = lane >> 3;
-  // tile row R j + 8 w + rr: swz_key = rr ^ ((R j / 8 + w) & 1) = rr ^ (w & 1), as R j / 8 is even
-  const int lchunk = (lane & 7) ^ rr ^ (wave & 1);
+  const int rr = lane / CPR;
+  const int lchunk = swz<RB>(T::RPW * wave + rr, lane % CPR);
   const uint8_t* src[CH];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const int row = R * j + 8 * wave + rr;
+    const int row = R * j + T::RPW * wave + rr;
     if (R * j < BM) {
       const int am = min(m0 + row, g.M - 1);  // rows past M re-read row M-1; never stored
       src[j] = reinterpret_cast<const uint8_t*>(g.a) + (int64_t)am * g.lda * E + lchunk * 16;
@@ -147,9 +163,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
     }
   }
   auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % STAGES) * T::STAGE + 8 * wave * kRowBytes;
+    uint8_t* st = smem + (kt % STAGES) * T::STAGE + T::RPW * wave * RB;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) dma16(src[j] + kt * kRowBytes, st + R * j * kRowBytes);
+    for (int j = 0; j < CH; ++j) dma16(src[j] + kt * RB, st + R * j * RB);
   };
 
   f32x16 acc[T::TM][T::TN];
@@ -170,18 +186,18 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
 
   auto compute = [&](int buf) {
     const uint8_t* sa = smem + buf * T::STAGE;
-    const uint8_t* sw = sa + BM * kRowBytes;
+    const uint8_t* sw = sa + BM * RB;
     if constexpr (!FP8) {
-      // 4 steps of K=16: lane group fg takes chunk 2*s + fg of each row
+      // RB / 32 steps of K=16: lane group fg takes chunk 2*s + fg of each row
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < RB / 32; ++s) {
         f16x8 af[T::TM], wf[T::TN];
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
-          af[i] = *reinterpret_cast<const f16x8*>(sa + arow[i] * kRowBytes + swz(arow[i], 2 * s + fg) * 16);
+          af[i] = *reinterpret_cast<const f16x8*>(sa + arow[i] * RB + swz<RB>(arow[i], 2 * s + fg) * 16);
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
-          wf[j] = *reinterpret_cast<const f16x8*>(sw + wrow[j] * kRowBytes + swz(wrow[j], 2 * s + fg) * 16);
+          wf[j] = *reinterpret_cast<const f16x8*>(sw + wrow[j] * RB + swz<RB>(wrow[j], 2 * s + fg) * 16);
 #pragma unroll
         for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -189,21 +205,21 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[j], af[i], acc[i][j], 0, 0, 0);
       }
     } else {
-      // 2 steps of K=64: lane group fg takes chunks 4*s + 2*fg and +1. The
-      // same K permutation is applied to both operands, so the sum is exact.
+      // RB / 64 steps of K=64: lane group fg takes chunks 4*s + 2*fg and +1.
+      // The same K permutation is applied to both operands, so the sum is exact.
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < RB / 64; ++s) {
         i32x8 af[T::TM], wf[T::TN];
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
-          i32x4 lo = *reinterpret_cast<const i32x4*>(sa + arow[i] * kRowBytes + swz(arow[i], 4 * s + 2 * fg) * 16);
-          i32x4 hi = *reinterpret_cast<const i32x4*>(sa + arow[i] * kRowBytes + swz(arow[i], 4 * s + 2 * fg + 1) * 16);
+          i32x4 lo = *reinterpret_cast<const i32x4*>(sa + arow[i] * RB + swz<RB>(arow[i], 4 * s + 2 * fg) * 16);
+          i32x4 hi = *reinterpret_cast<const i32x4*>(sa + arow[i] * RB + swz<RB>(arow[i], 4 * s + 2 * fg + 1) * 16);
           af[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) {
-          i32x4 lo = *reinterpret_cast<const i32x4*>(sw + wrow[j] * kRowBytes + swz(wrow[j], 4 * s + 2 * fg) * 16);
-          i32x4 hi = *reinterpret_cast<const i32x4*>(sw + wrow[j] * kRowBytes + swz(wrow[j], 4 * s + 2 * fg + 1) * 16);
+          i32x4 lo = *reinterpret_cast<const i32x4*>(sw + wrow[j] * RB + swz<RB>(wrow[j], 4 * s + 2 * fg) * 16);
+          i32x4 hi = *reinterpret_cast<const i32x4*>(sw + wrow[j] * RB + swz<RB>(wrow[j], 4 * s + 2 * fg + 1) * 16);
           wf[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
@@ -371,12 +387,13 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN)) void gemm_kernel(GemmAr
   }
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8>
+template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8, int RB = kRowBytes,
+          int MINW = 1>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
-  if (g.N % BN != 0) return hipErrorInvalidValue;  // every column tile must be whole
+  if (g.N % BN != 0 || (g.K * (FP8 ? 1 : 2)) % RB != 0) return hipErrorInvalidValue;  // whole tiles and slices
   dim3 grid((g.N / BN) * ((g.M + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, FP8, EPI, OUT_FP8>), grid,
-                     dim3(Tile<BM, BN, WM, WN>::THREADS), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, FP8, EPI, OUT_FP8, RB, MINW>), grid,
+                     dim3(Tile<BM, BN, WM, WN, RB>::THREADS), 0, s, g);
   return hipGetLastError();
 }
 
@@ -396,6 +413,16 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     // 256x256 tiles: not for the residual epilogue (its F32 staged tile
     // would not fit the LDS ring) nor the V-transposing one (a tile must not
     // straddle the V column boundary)
+    // GELU epilogue (MLP up, N % 128 == 0): 256x128 tiles of four waves
+    // (128x64 each) with a 3-stage ring of 64-byte K slices, 72 KiB of LDS, so
+    // two workgroups share a CU and one's VALU-heavy epilogue (bias, GELU,
+    // e4m3) runs beside the other's MFMA main loop (measured at 46,656 x
+    // 4,352 x 1,152: 2-7% faster than one 256x256 workgroup per CU, the same
+    // bits; slower for the residual and QKV epilogues).
+    if constexpr (EPI == EPI_BIAS_GELU) {
+      if (b.group_m == 0) b.group_m = 8;
+      return launch_cfg<256, 128, 128, 64, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
+    }
     if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV && EPI != EPI_QKV8)
       if (g.N % 256 == 0) {
         if (b.group_m == 0) b.group_m = 4;
