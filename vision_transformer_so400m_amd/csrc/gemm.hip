@@ -300,89 +300,106 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
   constexpr int SB = sizeof(SType);
   constexpr int SROW = BN * SB;  // staged bytes per row
   constexpr int SCH = SROW / 16;
-  constexpr int SWZ = (SCH < 16 ? SCH : 16) - 1;
-  static_assert(BM * SROW <= STAGES * T::STAGE, "the staged tile fits the LDS ring");
+  // chunk swizzle mask: the largest power of two <= 16 that divides the
+  // row's chunk count, so a swizzled chunk stays inside its row (a 384-byte
+  // e4m3 row has 24 chunks: mask 7)
+  constexpr int SWZ = (SCH % 16 == 0 ? 16 : SCH % 8 == 0 ? 8 : SCH % 4 == 0 ? 4 : SCH % 2 == 0 ? 2 : 1) - 1;
+  static_assert(SCH % (SWZ + 1) == 0, "swizzled chunks stay inside the row");
+  // A tile whose staged form exceeds the ring (the F32 residual tile of the
+  // widest tiles) is staged and stored in PASSES bands of PR rows; every
+  // 32-row block of a wave falls in one band.
+  constexpr int RING = STAGES * T::STAGE;
+  constexpr int PASSES = (BM * SROW + RING - 1) / RING;
+  constexpr int PR = BM / PASSES;
+  static_assert(BM % PASSES == 0 && PR % 32 == 0 && PR * SROW <= RING, "the staged bands fit the LDS ring");
   auto saddr = [&](int r, int byte) -> uint8_t* {
     return smem + r * SROW + ((((byte >> 4) ^ (r & SWZ)) << 4) | (byte & 15));
   };
-  __syncthreads();  // every wave is done with the ring (no transfer is outstanding)
-#pragma unroll
-  for (int i = 0; i < T::TM; ++i) {
-    const int r = wm * WM + i * 32 + fr;
-    const int m = m0 + r;
-#pragma unroll
-    for (int j = 0; j < T::TN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = wn * WN + j * 32 + 8 * q + 4 * fg;
-        const int n = n0 + c;
-        const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + n);
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * g.acc_scale + b[e];
-        if constexpr (EPI == EPI_BIAS_POS) {
-          const f32x4 p = *reinterpret_cast<const f32x4*>(g.pos + (int64_t)(m % g.pos_rows) * g.ldpos + n);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += p[e];
-        }
-        if constexpr (EPI == EPI_BIAS_GELU) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
-        }
-        if constexpr (SB == 4) {
-          *reinterpret_cast<f32x4*>(saddr(r, 4 * c)) = f32x4{v[0], v[1], v[2], v[3]};
-        } else if constexpr (SB == 2) {
-          *reinterpret_cast<f16x4*>(saddr(r, 2 * c)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
-        } else {
-          const float sc = EPI == EPI_QKV8 ? g.qk8_scale : g.out_scale;
-          *reinterpret_cast<uint32_t*>(saddr(r, c)) = pack4_e4m3(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if constexpr (EPI == EPI_QKV8) {
-    // e4m3 Q/K codes into head slots: 8 consecutive columns never cross a
-    // head (vt_dim % 8 == 0, n0 % 8 == 0), so each 8-byte group of a staged
-    // row is one 8-byte store; consecutive threads take consecutive groups
-    constexpr int G = BN / 8;
-#pragma unroll 4
-    for (int u = t; u < BM * G; u += T::THREADS) {
-      const int r = u / G;
-      const int c = (u - r * G) * 8;
-      const int m = m0 + r;
-      if (m >= g.M) continue;
-      const int n = n0 + c;
-      const int hh = (int)(((float)n + 0.5f) * g.vt_inv_dim);  // exact: n < 2^20, dim <= 2^10
-      const int dd = n - hh * g.vt_dim;
-      *reinterpret_cast<uint2*>(g.qk8 + (int64_t)m * g.qk8_ld + hh * g.qk8_pitch + dd) =
-          *reinterpret_cast<const uint2*>(saddr(r, c));
-    }
-    return;
-  }
   constexpr int OB = SB == 1 ? 1 : 2;
   constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
   constexpr int VPC = 16 / OB;       // values per output chunk
-#pragma unroll 4
-  for (int u = t; u < BM * OCH; u += T::THREADS) {
-    const int r = u / OCH;
-    const int c = (u - r * OCH) * VPC;
-    const int m = m0 + r;
-    if (m >= g.M) continue;
-    uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + ((int64_t)m * g.ldc + n0 + c) * OB;
-    if constexpr (SB == 4) {  // F32 staged, residual added here, F16 out
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(saddr(r, 4 * c));
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(saddr(r, 4 * c + 16));
-      const f16x8 rr = *reinterpret_cast<const f16x8*>(g.res + (int64_t)m * g.ldres + n0 + c);
-      f16x8 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] = (f16)(lo[e] + (float)rr[e]);
-        o[e + 4] = (f16)(hi[e] + (float)rr[e + 4]);
+  for (int pass = 0; pass < PASSES; ++pass) {
+    // every wave is done with the ring (no transfer is outstanding), or with
+    // the previous band's stores
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+      const int r = wm * WM + i * 32 + fr;  // tile row
+      if ((wm * WM + i * 32) / PR != pass) continue;
+      const int rs = r - pass * PR;  // row of the staged band
+      const int m = m0 + r;
+#pragma unroll
+      for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * WN + j * 32 + 8 * q + 4 * fg;
+          const int n = n0 + c;
+          const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + n);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * g.acc_scale + b[e];
+          if constexpr (EPI == EPI_BIAS_POS) {
+            const f32x4 p = *reinterpret_cast<const f32x4*>(g.pos + (int64_t)(m % g.pos_rows) * g.ldpos + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += p[e];
+          }
+          if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+          }
+          if constexpr (SB == 4) {
+            *reinterpret_cast<f32x4*>(saddr(rs, 4 * c)) = f32x4{v[0], v[1], v[2], v[3]};
+          } else if constexpr (SB == 2) {
+            *reinterpret_cast<f16x4*>(saddr(rs, 2 * c)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+          } else {
+            const float sc = EPI == EPI_QKV8 ? g.qk8_scale : g.out_scale;
+            *reinterpret_cast<uint32_t*>(saddr(rs, c)) = pack4_e4m3(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
+          }
+        }
       }
-      *reinterpret_cast<f16x8*>(dst) = o;
+    }
+    __syncthreads();
+    if constexpr (EPI == EPI_QKV8) {
+      // e4m3 Q/K codes into head slots: 8 consecutive columns never cross a
+      // head (vt_dim % 8 == 0, n0 % 8 == 0), so each 8-byte group of a staged
+      // row is one 8-byte store; consecutive threads take consecutive groups
+      constexpr int G = BN / 8;
+#pragma unroll 4
+      for (int u = t; u < PR * G; u += T::THREADS) {
+        const int rs = u / G;
+        const int c = (u - rs * G) * 8;
+        const int m = m0 + pass * PR + rs;
+        if (m >= g.M) continue;
+        const int n = n0 + c;
+        const int hh = (int)(((float)n + 0.5f) * g.vt_inv_dim);  // exact: n < 2^20, dim <= 2^10
+        const int dd = n - hh * g.vt_dim;
+        *reinterpret_cast<uint2*>(g.qk8 + (int64_t)m * g.qk8_ld + hh * g.qk8_pitch + dd) =
+            *reinterpret_cast<const uint2*>(saddr(rs, c));
+      }
     } else {
-      *reinterpret_cast<i32x4*>(dst) = *reinterpret_cast<const i32x4*>(saddr(r, c * SB));
+#pragma unroll 4
+      for (int u = t; u < PR * OCH; u += T::THREADS) {
+        const int rs = u / OCH;
+        const int c = (u - rs * OCH) * VPC;
+        const int m = m0 + pass * PR + rs;
+        if (m >= g.M) continue;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(g.c) + ((int64_t)m * g.ldc + n0 + c) * OB;
+        if constexpr (SB == 4) {  // F32 staged, residual added here, F16 out
+          const f32x4 lo = *reinterpret_cast<const f32x4*>(saddr(rs, 4 * c));
+          const f32x4 hi = *reinterpret_cast<const f32x4*>(saddr(rs, 4 * c + 16));
+          const f16x8 rr = *reinterpret_cast<const f16x8*>(g.res + (int64_t)m * g.ldres + n0 + c);
+          f16x8 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = (f16)(lo[e] + (float)rr[e]);
+            o[e + 4] = (f16)(hi[e] + (float)rr[e + 4]);
+          }
+          *reinterpret_cast<f16x8*>(dst) = o;
+        } else {
+          *reinterpret_cast<i32x4*>(dst) = *reinterpret_cast<const i32x4*>(saddr(rs, c * SB));
+        }
+      }
     }
   }
 }
@@ -422,6 +439,23 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     if constexpr (EPI == EPI_BIAS_GELU) {
       if (b.group_m == 0) b.group_m = 8;
       return launch_cfg<256, 128, 128, 64, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
+    }
+    // Long K (MLP down, K = 4352) or wide N (the fused QKV projection, 3456;
+    // the explicit MAP K/V, 2304): 192x384 tiles of eight waves (96x96
+    // each), 2 stages, 144 KiB of LDS. Per flop they move half the operand
+    // bytes of 128x128 tiles from L2 into LDS (A is re-read for 3 column
+    // blocks of 1152 instead of 9), which is what bounds these GEMMs: at
+    // 46,656 rows MLP down 280 -> 245 us and a 3456-wide projection 235-251 ->
+    // 222 us, the same bits. The residual tile is staged in two bands. Not
+    // for the out-projection (K = 1152: 729 tiles leave a long tail; 98 ->
+    // 105-113 us). A V-transposing tile must not straddle the V columns.
+    if constexpr (EPI == EPI_BIAS_RES || EPI == EPI_BIAS || EPI == EPI_QKV || EPI == EPI_QKV8) {
+      constexpr bool qkv = EPI == EPI_QKV || EPI == EPI_QKV8;
+      const bool fits = g.N % 384 == 0 && (!qkv || g.vt_col0 % 384 == 0);
+      if (fits && ((int64_t)g.K * (FP8 ? 1 : 2) >= 2048 || g.N >= 2304)) {
+        if (b.group_m == 0) b.group_m = 8;
+        return launch_cfg<192, 384, 96, 96, 2, FP8, EPI, OUT_FP8>(b, s);
+      }
     }
     if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV && EPI != EPI_QKV8)
       if (g.N % 256 == 0) {
