@@ -74,12 +74,24 @@ __device__ __forceinline__ float half_other(float v) {
 // z = sqrt(2/pi) x (1 + 0.044715 x^2): one exp2 and one reciprocal (both
 // hardware approximations, ~1 ulp of F32), no IEEE division. Large negative x
 // gives exp2 -> inf and x * rcp(inf) = -0; large positive x gives x.
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float k = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
-  const float x2 = x * x;
-  const float z = x * fmaf(0.044715f, x2, 1.0f);
-  const float e = __builtin_amdgcn_exp2f(k * z);
-  return x * __builtin_amdgcn_rcpf(1.0f + e);
+//
+// gelu_tanh_scaled takes xs = sc * x for a power of two sc (the e4m3 output
+// scale, or 1) and returns sc * gelu(x): with the exponent -2 z log2(e)
+// written as xs * (k1 + k3 xs^2), k1 = -2 sqrt(2/pi) log2(e) / sc and
+// k3 = k1 * 0.044715 / sc^2, the scale costs no instruction per element.
+constexpr float kGeluExp2K = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+constexpr float kGeluCubic = 0.044715f;
+
+struct GeluConsts {
+  float k1, k3;
+};
+__device__ __forceinline__ GeluConsts gelu_consts(float sc) {
+  const float k1 = kGeluExp2K / sc;
+  return {k1, k1 * kGeluCubic / (sc * sc)};
+}
+__device__ __forceinline__ float gelu_tanh_scaled(float xs, GeluConsts k) {
+  const float e = __builtin_amdgcn_exp2f(xs * fmaf(k.k3, xs * xs, k.k1));
+  return xs * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // ------------------------------------------------------------------ GEMM

@@ -318,27 +318,38 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
   constexpr int OB = SB == 1 ? 1 : 2;
   constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
   constexpr int VPC = 16 / OB;       // values per output chunk
+  // The GELU epilogue with e4m3 output applies its power-of-two output scale
+  // to the GELU input (exactly) and to the GELU constants instead of to
+  // every output.
+  constexpr bool GELU8 = EPI == EPI_BIAS_GELU && SB == 1;
+  const float pre = GELU8 ? g.out_scale : 1.0f;
+  const float vscale = g.acc_scale * pre;
+  const GeluConsts gk = gelu_consts(pre);
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
     // every wave is done with the ring (no transfer is outstanding), or with
     // the previous band's stores
     __syncthreads();
+    // column pieces outermost so each lane's bias quad is loaded (and
+    // scaled) once for all its row blocks
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
-      const int r = wm * WM + i * 32 + fr;  // tile row
-      if ((wm * WM + i * 32) / PR != pass) continue;
-      const int rs = r - pass * PR;  // row of the staged band
-      const int m = m0 + r;
+    for (int j = 0; j < T::TN; ++j) {
 #pragma unroll
-      for (int j = 0; j < T::TN; ++j) {
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * WN + j * 32 + 8 * q + 4 * fg;
+        const int n = n0 + c;
+        f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + n);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = wn * WN + j * 32 + 8 * q + 4 * fg;
-          const int n = n0 + c;
-          const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + n);
+        for (int e = 0; e < 4; ++e) b[e] *= pre;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+          const int r = wm * WM + i * 32 + fr;  // tile row
+          if ((wm * WM + i * 32) / PR != pass) continue;
+          const int rs = r - pass * PR;  // row of the staged band
+          const int m = m0 + r;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * g.acc_scale + b[e];
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * vscale + b[e];
           if constexpr (EPI == EPI_BIAS_POS) {
             const f32x4 p = *reinterpret_cast<const f32x4*>(g.pos + (int64_t)(m % g.pos_rows) * g.ldpos + n);
 #pragma unroll
@@ -346,12 +357,14 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
           }
           if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+            for (int e = 0; e < 4; ++e) v[e] = gelu_tanh_scaled(v[e], gk);
           }
           if constexpr (SB == 4) {
             *reinterpret_cast<f32x4*>(saddr(rs, 4 * c)) = f32x4{v[0], v[1], v[2], v[3]};
           } else if constexpr (SB == 2) {
             *reinterpret_cast<f16x4*>(saddr(rs, 2 * c)) = f16x4{(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+          } else if constexpr (GELU8) {
+            *reinterpret_cast<uint32_t*>(saddr(rs, c)) = pack4_e4m3(v[0], v[1], v[2], v[3]);
           } else {
             const float sc = EPI == EPI_QKV8 ? g.qk8_scale : g.out_scale;
             *reinterpret_cast<uint32_t*>(saddr(rs, c)) = pack4_e4m3(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
