@@ -429,16 +429,17 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
 
 template <bool FP8, int EPI, bool OUT_FP8>
 hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
-  // Tile choice measured on the batch-64 shapes (M = 46,656): N divisible by
-  // 256 takes 256x256 tiles of eight waves (128x64 each, one workgroup per
-  // CU); the others take 128x128 tiles of eight waves (64x32 each) with two
-  // LDS stages, two workgroups per CU. Small M falls back to smaller tiles
-  // that still fill the 256 CUs.
+  // Tile choice measured on the batch-64 shapes (M = 46,656): the GELU
+  // epilogue takes 256x128 tiles, long-K or wide residual/QKV GEMMs 192x384,
+  // other N divisible by 256 256x256 tiles of eight waves (128x64 each, one
+  // workgroup per CU), the rest 128x128 tiles of eight waves (64x32 each)
+  // with two LDS stages, two workgroups per CU. Small M falls back to
+  // smaller tiles that still fill the 256 CUs.
   const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
   if (tiles_128 >= 1024) {
     // Large grids walk tiles in bands of row blocks (tile_of) unless the
-    // caller chose a band: 4 row blocks of 256, 8 of 128 (measured at
-    // 46,656 rows: 1-3% over row-block-major order).
+    // caller chose a band: 4 row blocks for 256x256 tiles, 8 for the others
+    // (measured at 46,656 rows: 1-3% over row-block-major order).
     GemmArgs b = g;
     // 256x256 tiles: not for the residual epilogue (its F32 staged tile
     // would not fit the LDS ring) nor the V-transposing one (a tile must not
