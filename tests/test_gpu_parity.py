@@ -504,20 +504,22 @@ def check_stages_rows(model, wt, x, dims, fp8, batch, rows):
 
 
 def _band_rows(M):
-    """Row blocks at the first tile, the first tile-band boundary (1,024 rows:
-    8 row blocks of 128, 4 of 256), the middle and the last (partial) tile,
-    and the image boundary 728 | 729."""
-    blocks = [range(0, 128), range(960, 1088), range(M // 2 - 64, M // 2 + 64), range(M - 128, M),
-              range(720, 740)]
+    """Row blocks at the first tile, the first tile-band boundary of each
+    large-grid tile height (bands of 8 row blocks: 1,024 rows of 128-row
+    tiles, 1,536 of 192, 2,048 of 256), the middle and the last (partial)
+    tile, and the image boundary 728 | 729."""
+    blocks = [range(0, 128), range(960, 1088), range(1472, 1600), range(1984, 2112),
+              range(M // 2 - 64, M // 2 + 64), range(M - 128, M), range(720, 740)]
     return sorted({r for blk in blocks for r in blk if 0 <= r < M})
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
 def test_b64_layer0_stages_on_sampled_row_blocks(V, fp8):
-    """The batch-64 launch shapes (8-wave 128x128 and 256x256 tiles, banded
-    tile order, the V-transposing and residual epilogues) element by element
-    on sampled row blocks, at one layer (stage capture runs the batch on one
-    stream, so every launch covers all 46,656 rows)."""
+    """The batch-64 launch shapes (192x384 tiles for QKV and MLP-down,
+    256x128 for MLP-up, 128x128 for the out-projection, banded tile order,
+    the V-transposing and residual epilogues) element by element on sampled
+    row blocks, at one layer (stage capture runs the batch on one stream, so
+    every launch covers all 46,656 rows)."""
     dims = S.SO400M.with_depth(1)
     _flush(f"B=64 layer-0 stages on sampled rows, fp8={fp8}")
     model, wt = make_model(V, dims, 2, max_batch=64, fp8=fp8)
