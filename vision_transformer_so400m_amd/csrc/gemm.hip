@@ -43,13 +43,14 @@ struct Tile {
   static constexpr int WAVES_M = BM / WM;
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
-  static_assert(RB == 64 || RB == 128, "64- or 128-byte K slices");
+  static_assert(RB == 64 || RB == 128 || RB == 256, "64-, 128- or 256-byte K slices");
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int TM = WM / 32;
   static constexpr int TN = WN / 32;
   static constexpr int RPW = 1024 / RB;             // tile rows one wave's 1 KiB transfer fills
   static constexpr int ROWS_PER_ROUND = RPW * WAVES;  // tile rows one DMA round fills
   static_assert(BM % ROWS_PER_ROUND == 0 && BN % ROWS_PER_ROUND == 0, "whole DMA rounds");
+  static_assert(ROWS_PER_ROUND % 16 == 0, "a round's rows share their swizzle keys");
   static constexpr int STAGE = (BM + BN) * RB;
 };
 
@@ -58,11 +59,13 @@ struct Tile {
 // bytes. 128-byte rows: two rows span all banks, so (row & 1) picks the half
 // and the chunk must differ across the 8 rows of each parity: chunk ^ (row &
 // 7) ^ ((row >> 3) & 1). 64-byte rows: four rows span all banks, so the chunk
-// must differ across rows r, r+4, r+8, r+12: chunk ^ ((row >> 2) & 3). Both
-// are bijections on the chunks of any row.
+// must differ across rows r, r+4, r+8, r+12: chunk ^ ((row >> 2) & 3).
+// 256-byte rows: one row spans all banks, so the chunk must differ across the
+// 16 rows: chunk ^ (row & 15). All are bijections on the chunks of any row.
 template <int RB = kRowBytes>
 __device__ __forceinline__ int swz_key(int row) {
-  if constexpr (RB == 128) return (row & 7) ^ ((row >> 3) & 1);
+  if constexpr (RB == 256) return row & 15;
+  else if constexpr (RB == 128) return (row & 7) ^ ((row >> 3) & 1);
   else return (row >> 2) & 3;
 }
 template <int RB = kRowBytes>
@@ -485,7 +488,19 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // keeps one more slice in flight (measured: 15.0 -> 13.4 us for 729 x 1152
   // x 4352, 6.0 -> 5.6 us for K = 1152; larger grids gain nothing from it).
   const long tiles_64 = (long)((g.M + 63) / 64) * (g.N / 64);
-  if (tiles_64 < 512) return launch_cfg<64, 64, 32, 32, 4, FP8, EPI, OUT_FP8>(g, s);
+  // A grid of at most one 64x64 workgroup per CU with a long K (MLP down at
+  // batch 1, K = 4352) takes 256-byte slices: half the slices, and with them
+  // half the per-slice waits and barriers that make up its critical path
+  // (729 x 1152 x 4352: e4m3 16.4 -> 14.8 us, F16 27.0 -> 24.9 us, the same
+  // bits: the K order of every output is unchanged). Their 128 KiB ring
+  // leaves room for one workgroup per CU, so larger grids (1458 rows: 20.4
+  // -> 24.6 us) and short K (1152: up to 30% slower) keep 128-byte slices.
+  if (tiles_64 < 512) {
+    const int64_t kb = (int64_t)g.K * (FP8 ? 1 : 2);
+    if (tiles_64 <= 256 && kb >= 4096 && kb % 256 == 0)
+      return launch_cfg<64, 64, 32, 32, 4, FP8, EPI, OUT_FP8, 256>(g, s);
+    return launch_cfg<64, 64, 32, 32, 4, FP8, EPI, OUT_FP8>(g, s);
+  }
   // Between the two: 128x64 tiles of four waves (64x32 each), three stages.
   // Measured with every launch reading its weights cold from HBM (as the
   // layers of one small-batch call do), against 64x64 tiles with three
