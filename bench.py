@@ -14,8 +14,10 @@ kernel from a second timed pass of the same calls with events around that
 class's launches (launch events make the library run the batch unsplit on
 one stream, so every launch covers the whole batch and its duration is the
 kernel's own), the attention workload alone ([32, 729, 16 x 72]) against its
-MFMA and HBM floors, the F16 27-layer latency at batch 1 and 2, and a CPU
-baseline (the FP32 oracle on whole images of the input, on the host cores).
+MFMA and HBM floors, the F16 latency of 27 layers + MAP at batch 1 and 2
+and of one layer + MAP at batch 1 and 8 (each with its fraction of the dense
+F16 MFMA peak), and a CPU baseline (the FP32 oracle on whole images of the
+input, on the host cores).
 
   python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -164,23 +166,35 @@ def attention_alone(V, steps=30):
             "includes": "the V transpose into the staging buffer and the attention kernel"}
 
 
-def f16_latency(V, steps):
-    """Latency of the 27-layer model with F16 GEMM operands (weights and
-    pixels seed 1) at batch 1 and 2."""
+def rate(d, layers, batch, ms, fp8=False):
+    """ms per call -> images/s and the algorithmic rate against the dense
+    MFMA peak of the GEMM operand type (small batches are latency-bound; the
+    fraction is reported all the same)."""
+    tf = algorithmic_flops_per_image(d, layers) * batch / (ms / 1e3) / 1e12
+    peak = PEAK["fp8_mfma_tflops"] if fp8 else PEAK["f16_mfma_tflops"]
+    return {"ms": round(ms, 4), "images_per_s": round(batch / ms * 1e3, 2), "tflops": round(tf, 2),
+            "frac_of_peak": round(tf / peak, 4)}
+
+
+def f16_latency(V, steps, layers=27, seed=1, batches=(1, 2)):
+    """Latency of the model with F16 GEMM operands at small batches: 27
+    layers + MAP (weights and pixels seed 1) at batch 1 and 2, or one layer +
+    MAP (seed 0) at batch 1 and 8."""
     import torch
 
     import synthetic as S
-    d = S.SO400M
-    wt = S.make_weights(d, 1)
-    model = V.Model(S.pack_blob(d, wt), max_batch=2, fp8=False)
+    d = S.SO400M.with_depth(layers)
+    wt = S.make_weights(d, seed)
+    model = V.Model(S.pack_blob(d, wt), max_batch=max(batches), fp8=False)
     del wt
-    x = torch.from_numpy(S.make_pixels(d, 2, 1)).cuda()
-    res = {"workload": "27 layers + MAP, F16 GEMM operands, seed 1"}
-    for b in (1, 2):
+    x = torch.from_numpy(S.make_pixels(d, max(batches), seed)).cuda()
+    res = {"workload": f"{layers} layer{'s' if layers > 1 else ''} + MAP, F16 GEMM operands, seed {seed}",
+           "peak": "dense F16 MFMA, 2.5 PF/s"}
+    for b in batches:
         xb = x[:b].contiguous()
         o = torch.empty((b, 1, d.width), dtype=torch.float16, device="cuda")
         ms = time_calls(model, xb, o, steps, warmup=5)
-        res[f"b{b}"] = {"ms": round(ms, 4), "images_per_s": round(b / ms * 1e3, 2)}
+        res[f"b{b}"] = rate(d, layers, b, ms)
     model.close()
     return res
 
@@ -401,6 +415,7 @@ def main():
     del x, out
     c2 = attention_alone(V)
     c3 = f16_latency(V, args.b1_steps)
+    c01 = f16_latency(V, args.b1_steps, layers=1, seed=0, batches=(1, 8))
 
     line = {
         "metric": "images/sec, SigLIP So400m/14 378px 27-layer at B=1 and B=64; % MFMA peak",
@@ -426,9 +441,10 @@ def main():
         "event_ms_per_step": round(ev_ms, 4),
         "unsplit_ms_per_step": round(unsplit_ms, 4),
         "deterministic_across_steps": deterministic,
-        "b1": {"ms": round(b1_ms, 4), "images_per_s": round(1e3 / b1_ms, 2),
-               "workload": "same model and weights, batch 1"},
+        "b1": {**rate(d, d.depth, 1, b1_ms, fp8=cfg["fp8"]),
+               "workload": "same model and weights, batch 1", "peak": "dense e4m3 MFMA, 5.0 PF/s"},
         "f16_27layer_latency": c3,
+        "f16_1layer_latency": c01,
         "attention_b32_t729": c2,
         "kernels": kernels,
         "roofline": roofline,
