@@ -16,16 +16,19 @@
 //
 // Tiling: a workgroup of 4 or 8 waves owns a BM x BN output tile and walks K in
 // 128-byte slices (64 F16 or 128 e4m3 values per row; 64-byte slices for the
-// MLP-up tile). Slices go global ->
-// LDS directly (global_load_lds_dwordx4) into a ring of STAGES buffers, so the
-// loads of the next slices are in flight while one is multiplied. LDS rows are
-// 128 bytes with the 16-byte chunk index XOR-swizzled (swz below), so the 16
-// lanes that read one chunk of 16 consecutive rows hit distinct banks.
+// MLP-up tile, 256-byte slices for one-round small grids with a long K).
+// Slices go global -> LDS directly (global_load_lds_dwordx4) into a ring of
+// STAGES buffers, so the loads of the next slices are in flight while one is
+// multiplied. The 16-byte chunk index of each LDS row is XOR-swizzled (swz
+// below), so the 16 lanes that read one chunk of 16 consecutive rows hit
+// distinct banks.
 //
 // The MFMA is issued with the weight fragment as its first operand, so the
 // hardware's 32x32 result holds, per lane, one activation row m and four
-// consecutive output columns n per register quad: the epilogue reads bias
-// and residual and writes the output 4 columns (8 bytes F16) at a time.
+// consecutive output columns n per register quad. The epilogue stages these
+// values through the idle LDS ring and writes whole 16-byte chunks of output
+// rows (the V^T columns of the QKV projection are stored transposed straight
+// from registers).
 #include "common.h"
 
 #include <type_traits>
@@ -235,6 +238,45 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
     }
   };
 
+  using SType = typename StageType<EPI, OUT_FP8>::type;
+  constexpr int SB = sizeof(SType);
+  constexpr int SROW = BN * SB;  // staged bytes per row
+  constexpr int SCH = SROW / 16;
+  // chunk swizzle mask: the largest power of two <= 16 that divides the
+  // row's chunk count, so a swizzled chunk stays inside its row (a 384-byte
+  // e4m3 row has 24 chunks: mask 7)
+  constexpr int SWZ = (SCH % 16 == 0 ? 16 : SCH % 8 == 0 ? 8 : SCH % 4 == 0 ? 4 : SCH % 2 == 0 ? 2 : 1) - 1;
+  static_assert(SCH % (SWZ + 1) == 0, "swizzled chunks stay inside the row");
+  // A tile whose staged form exceeds the ring (the F32 residual tile of the
+  // widest tiles) is staged and stored in PASSES bands of PR rows; every
+  // 32-row block of a wave falls in one band.
+  constexpr int RING = STAGES * T::STAGE;
+  constexpr int PASSES = (BM * SROW + RING - 1) / RING;
+  constexpr int PR = BM / PASSES;
+  static_assert(BM % PASSES == 0 && PR % 32 == 0 && PR * SROW <= RING, "the staged bands fit the LDS ring");
+  constexpr int OB = SB == 1 ? 1 : 2;
+  constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
+  constexpr int VPC = 16 / OB;       // values per output chunk
+  // Residual prefetch: where the residual tile is stored in one pass with at
+  // most four 16-byte chunks per thread (the 128x128 and smaller residual
+  // tiles), the residual chunks this thread adds in the epilogue are loaded
+  // here, so their latency hides behind the main loop instead of following
+  // it. The residual rows are read and written by this workgroup only, so
+  // reading them early is safe in place too. These loads are older than every
+  // slice transfer, so the slice waits below also cover them.
+  constexpr int NPF = (EPI == EPI_BIAS_RES && PASSES == 1 && (PR * OCH) % T::THREADS == 0 &&
+                       PR * OCH / T::THREADS <= 4) ? PR * OCH / T::THREADS : 0;
+  f16x8 rpf[NPF > 0 ? NPF : 1];
+  if constexpr (NPF > 0) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int u = t + i * T::THREADS;
+      const int rs = u / OCH;
+      const int m = m0 + rs;
+      if (m < g.M) rpf[i] = *reinterpret_cast<const f16x8*>(g.res + (int64_t)m * g.ldres + n0 + (u - rs * OCH) * VPC);
+    }
+  }
+
   // prologue: the first STAGES-1 slices in flight
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
@@ -299,28 +341,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
   // chunks, adding the residual there from 16-byte loads. Staged rows are
   // swizzled in 16-byte chunks by row so the column-wise writes of 16 rows
   // hit distinct banks.
-  using SType = typename StageType<EPI, OUT_FP8>::type;
-  constexpr int SB = sizeof(SType);
-  constexpr int SROW = BN * SB;  // staged bytes per row
-  constexpr int SCH = SROW / 16;
-  // chunk swizzle mask: the largest power of two <= 16 that divides the
-  // row's chunk count, so a swizzled chunk stays inside its row (a 384-byte
-  // e4m3 row has 24 chunks: mask 7)
-  constexpr int SWZ = (SCH % 16 == 0 ? 16 : SCH % 8 == 0 ? 8 : SCH % 4 == 0 ? 4 : SCH % 2 == 0 ? 2 : 1) - 1;
-  static_assert(SCH % (SWZ + 1) == 0, "swizzled chunks stay inside the row");
-  // A tile whose staged form exceeds the ring (the F32 residual tile of the
-  // widest tiles) is staged and stored in PASSES bands of PR rows; every
-  // 32-row block of a wave falls in one band.
-  constexpr int RING = STAGES * T::STAGE;
-  constexpr int PASSES = (BM * SROW + RING - 1) / RING;
-  constexpr int PR = BM / PASSES;
-  static_assert(BM % PASSES == 0 && PR % 32 == 0 && PR * SROW <= RING, "the staged bands fit the LDS ring");
   auto saddr = [&](int r, int byte) -> uint8_t* {
     return smem + r * SROW + ((((byte >> 4) ^ (r & SWZ)) << 4) | (byte & 15));
   };
-  constexpr int OB = SB == 1 ? 1 : 2;
-  constexpr int OCH = BN * OB / 16;  // 16-byte output chunks per row
-  constexpr int VPC = 16 / OB;       // values per output chunk
   // The GELU epilogue with e4m3 output applies its power-of-two output scale
   // to the GELU input (exactly) and to the GELU constants instead of to
   // every output.
@@ -392,6 +415,26 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
         const int dd = n - hh * g.vt_dim;
         *reinterpret_cast<uint2*>(g.qk8 + (int64_t)m * g.qk8_ld + hh * g.qk8_pitch + dd) =
             *reinterpret_cast<const uint2*>(saddr(rs, c));
+      }
+    } else if constexpr (NPF > 0) {
+      // the residual tile with its prefetched chunks (PASSES == 1, every
+      // thread owns NPF whole chunks)
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) {
+        const int u = t + i * T::THREADS;
+        const int rs = u / OCH;
+        const int c = (u - rs * OCH) * VPC;
+        const int m = m0 + rs;
+        if (m >= g.M) continue;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(saddr(rs, 4 * c));
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(saddr(rs, 4 * c + 16));
+        f16x8 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = (f16)(lo[e] + (float)rpf[i][e]);
+          o[e + 4] = (f16)(hi[e] + (float)rpf[i][e + 4]);
+        }
+        *reinterpret_cast<f16x8*>(reinterpret_cast<f16*>(g.c) + (int64_t)m * g.ldc + n0 + c) = o;
       }
     } else {
 #pragma unroll 4
