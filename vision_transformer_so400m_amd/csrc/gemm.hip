@@ -45,7 +45,7 @@ struct Tile {
   static constexpr int WAVES_N = BN / WN;
   static constexpr int WAVES_M = BM / WM;
   static constexpr int WAVES = WAVES_M * WAVES_N;
-  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
+  static_assert(WAVES == 4 || WAVES == 8 || WAVES == 12, "four, eight or twelve waves per workgroup");
   static_assert(RB == 64 || RB == 128 || RB == 256, "64-, 128- or 256-byte K slices");
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int TM = WM / 32;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
   // ---- epilogue: lane holds row m = tile row + fr, columns 8q + 4fg + (0..3)
   if constexpr (EPI == EPI_QKV || EPI == EPI_QKV8) {
     if (n0 + wn * WN >= g.vt_col0) {
-      // V columns (whole waves: vt_col0 is a multiple of 128): 4 consecutive
+      // V columns (whole tiles: vt_col0 is a multiple of the tile width): 4 consecutive
       // dims of one head written transposed. The 32 lanes of a half-wave hold
       // 32 consecutive tokens, so each store covers 64 (F16) or 32 (e4m3)
       // contiguous bytes of a V^T row.
@@ -501,20 +501,24 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
       return launch_cfg<256, 128, 128, 64, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
     }
     // Long K (MLP down, K = 4352) or wide N (the fused QKV projection, 3456;
-    // the explicit MAP K/V, 2304): 192x384 tiles of eight waves (96x96
-    // each), 2 stages, 144 KiB of LDS. Per flop they move half the operand
-    // bytes of 128x128 tiles from L2 into LDS (A is re-read for 3 column
-    // blocks of 1152 instead of 9), which is what bounds these GEMMs: at
-    // 46,656 rows MLP down 280 -> 245 us and a 3456-wide projection 235-251 ->
-    // 222 us, the same bits. The residual tile is staged in two bands. Not
-    // for the out-projection (K = 1152: 729 tiles leave a long tail; 98 ->
-    // 105-113 us). A V-transposing tile must not straddle the V columns.
+    // the explicit MAP K/V, 2304): 192x384 tiles, 2 stages, 144 KiB of LDS.
+    // Per flop they move half the operand bytes of 128x128 tiles from L2
+    // into LDS (A is re-read for 3 column blocks of 1152 instead of 9), which
+    // is what bounds these GEMMs: at 46,656 rows MLP down 280 -> 245 us and a
+    // 3456-wide projection 235-251 -> 222 us with eight waves of 96x96, the
+    // same bits. Twelve waves of 96x64 (164-167 VGPRs, three waves per SIMD
+    // instead of two, to cover the slice waits and the epilogue) take a
+    // 3456-wide projection from 221-231 to 207-215 us and MLP down from
+    // ~248 to 233-251 us, the same bits. The residual tile is staged in two
+    // bands. Not for the out-projection (K = 1152: 729 tiles leave a long
+    // tail; 98 -> 105-113 us). A V-transposing tile must not straddle the V
+    // columns.
     if constexpr (EPI == EPI_BIAS_RES || EPI == EPI_BIAS || EPI == EPI_QKV || EPI == EPI_QKV8) {
       constexpr bool qkv = EPI == EPI_QKV || EPI == EPI_QKV8;
       const bool fits = g.N % 384 == 0 && (!qkv || g.vt_col0 % 384 == 0);
       if (fits && ((int64_t)g.K * (FP8 ? 1 : 2) >= 2048 || g.N >= 2304)) {
         if (b.group_m == 0) b.group_m = 8;
-        return launch_cfg<192, 384, 96, 96, 2, FP8, EPI, OUT_FP8>(b, s);
+        return launch_cfg<192, 384, 96, 64, 2, FP8, EPI, OUT_FP8>(b, s);
       }
     }
     if constexpr (EPI != EPI_BIAS_RES && EPI != EPI_QKV && EPI != EPI_QKV8)
