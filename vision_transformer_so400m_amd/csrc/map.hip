@@ -227,19 +227,25 @@ __global__ __launch_bounds__(kPoolThreads) void map_pool_kernel(const f16* __res
   }
 }
 
-// One workgroup per (head, group of 4 images). wvt holds W_v transposed per
-// head: wvt[(h*D + d) * width + k] = W_v[k][h*D + d]. Thread (kc, d) =
-// (tid / D, tid % D) sums the K chunk [kc width/8, (kc+1) width/8) for the
-// 4 images (zbar rows staged in LDS); the 8 chunks are added in LDS.
+// One workgroup per (head, quarter of the head's D outputs, group of 4
+// images). wvt holds W_v transposed per head: wvt[(h*D + d) * width + k] =
+// W_v[k][h*D + d]. Thread (kc, d) = (tid / (D/4), tid % (D/4)) sums the K
+// chunk [kc width/32, (kc+1) width/32) for the 4 images (zbar rows staged in
+// LDS); the 32 chunks are added in LDS in chunk order. Short per-thread
+// chains and 4x the workgroups of one per head: at batch 1 the launch is
+// bound by the latency of each thread's chain of loads.
 constexpr int kVprojImages = 4;
-constexpr int kVprojChunks = 8;
+constexpr int kVprojChunks = 32;
+constexpr int kVprojSplit = 4;  // output groups per head
 
 template <bool OUT_FP8>
 __global__ __launch_bounds__(1024) void map_vproj_kernel(const float* __restrict__ zbar, const float* __restrict__ wvt,
                                                          const float* __restrict__ bv, int width, int D, int batch,
                                                          void* __restrict__ o, int64_t ldo, float out_scale) {
-  extern __shared__ float sm[];  // zbar rows [kVprojImages][width], then partials [kVprojChunks][kVprojImages][D]
-  const int h = blockIdx.x;
+  extern __shared__ float sm[];  // zbar rows [kVprojImages][width], then partials [kVprojChunks][kVprojImages][DD]
+  const int h = blockIdx.x / kVprojSplit;
+  const int DD = D / kVprojSplit;  // outputs of this workgroup: dims dg*DD .. dg*DD + DD - 1 of head h
+  const int dg = blockIdx.x - h * kVprojSplit;
   const int b0 = blockIdx.y * kVprojImages;
   const int nb = min(kVprojImages, batch - b0);
   for (int i = threadIdx.x; i < kVprojImages * width; i += blockDim.x) {
@@ -247,12 +253,12 @@ __global__ __launch_bounds__(1024) void map_vproj_kernel(const float* __restrict
     sm[i] = bi < nb ? zbar[((int64_t)(b0 + bi) * kMapHeads + h) * width + (i - bi * width)] : 0.f;
   }
   __syncthreads();
-  const int kc = threadIdx.x / D;
-  const int d = threadIdx.x - kc * D;
+  const int kc = threadIdx.x / DD;
+  const int d = threadIdx.x - kc * DD;
   const int chunk = width / kVprojChunks;
   float acc[kVprojImages] = {0.f, 0.f, 0.f, 0.f};
   if (kc < kVprojChunks) {
-    const float* wr = wvt + (int64_t)(h * D + d) * width + kc * chunk;
+    const float* wr = wvt + (int64_t)(h * D + dg * DD + d) * width + kc * chunk;
     const float* zr = sm + kc * chunk;
 #pragma unroll 4
     for (int k = 0; k < chunk; k += 4) {
@@ -267,15 +273,15 @@ __global__ __launch_bounds__(1024) void map_vproj_kernel(const float* __restrict
   float* red = sm + kVprojImages * width;
   if (kc < kVprojChunks)
 #pragma unroll
-    for (int bi = 0; bi < kVprojImages; ++bi) red[(kc * kVprojImages + bi) * D + d] = acc[bi];
+    for (int bi = 0; bi < kVprojImages; ++bi) red[(kc * kVprojImages + bi) * DD + d] = acc[bi];
   __syncthreads();
-  if (threadIdx.x < kVprojImages * D) {
-    const int bi = threadIdx.x / D, dd = threadIdx.x - bi * D;
+  if (threadIdx.x < kVprojImages * DD) {
+    const int bi = threadIdx.x / DD, dd = threadIdx.x - bi * DD;
     if (bi < nb) {
-      float v = bv[h * D + dd];
+      float v = bv[h * D + dg * DD + dd];
 #pragma unroll
-      for (int c = 0; c < kVprojChunks; ++c) v += red[(c * kVprojImages + bi) * D + dd];
-      const int64_t at = (int64_t)(b0 + bi) * ldo + h * D + dd;
+      for (int c = 0; c < kVprojChunks; ++c) v += red[(c * kVprojImages + bi) * DD + dd];
+      const int64_t at = (int64_t)(b0 + bi) * ldo + h * D + dg * DD + dd;
       if constexpr (OUT_FP8)
         reinterpret_cast<uint8_t*>(o)[at] = (uint8_t)(cvt_pk_e4m3(v * out_scale, 0.f, 0u, false) & 0xFF);
       else
@@ -340,7 +346,8 @@ __global__ __launch_bounds__(256) void map_wv_transpose_kernel(const float* __re
 
 bool map_fold_supported(int width, int heads, int head_dim, int tokens) {
   return heads >= 1 && heads <= kMapHeads && width % 128 == 0 && width <= 4096 && tokens >= 1 &&
-         tokens <= kMaxTokens && head_dim >= 4 && head_dim % 4 == 0 && head_dim * kVprojChunks <= 1024 &&
+         tokens <= kMaxTokens && head_dim >= 4 && head_dim % kVprojSplit == 0 &&
+         head_dim / kVprojSplit * kVprojChunks <= 1024 &&
          heads * head_dim == width;
 }
 
@@ -364,9 +371,10 @@ hipError_t launch_map_fold(const f16* z, int64_t ldz, const f16* u_hi, const f16
                      scores, tokens, heads, zbar, width);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)heads, (unsigned)((batch + kVprojImages - 1) / kVprojImages));
-  const dim3 block((unsigned)(head_dim * kVprojChunks));
-  const size_t lds = ((size_t)kVprojImages * width + (size_t)kVprojChunks * kVprojImages * head_dim) * sizeof(float);
+  const dim3 grid((unsigned)(heads * kVprojSplit), (unsigned)((batch + kVprojImages - 1) / kVprojImages));
+  const dim3 block((unsigned)(head_dim / kVprojSplit * kVprojChunks));
+  const size_t lds =
+      ((size_t)kVprojImages * width + (size_t)kVprojChunks * kVprojImages * (head_dim / kVprojSplit)) * sizeof(float);
   if (out_fp8)
     hipLaunchKernelGGL(map_vproj_kernel<true>, grid, block, lds, s, zbar, wvt, bv, width, head_dim, batch, o, ldo,
                        out_scale);
