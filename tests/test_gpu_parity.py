@@ -250,6 +250,26 @@ def test_attention_c2_full_size_all_pairs(V):
     np.testing.assert_array_equal(out2.cpu().numpy().view(np.uint16), o.view(np.uint16))
 
 
+@pytest.mark.parametrize("d", [72, 64, 80])
+def test_attention_small_batch_kernel_matches_full_grid_kernel_bitwise(V, d):
+    """A grid of one round (here one image x 16 heads x 729 tokens) runs the
+    16-query kernel, a larger one (four images) the 32-query kernel: the same
+    image must give the same bits, and both meet the oracle's bar."""
+    b, t, heads = 4, 729, 16
+    w = heads * d
+    _flush(f"attention one-round vs full-grid kernel d={d}")
+    rng = np.random.default_rng(300 + d)
+    q, k, v = (rng.standard_normal((b, t, w), dtype=np.float32).astype(np.float16) for _ in range(3))
+    scale = 1 / math.sqrt(d)
+    full = V.attention(*(torch.from_numpy(a).cuda() for a in (q, k, v)), heads, d, scale)
+    one = V.attention(*(torch.from_numpy(a[2:3].copy()).cuda() for a in (q, k, v)), heads, d, scale)
+    torch.cuda.synchronize()
+    full, one = full.cpu().numpy(), one.cpu().numpy()
+    np.testing.assert_array_equal(one[0].view(np.uint16), full[2].view(np.uint16))
+    ref = _attn_ref(q[2:3], k[2:3], v[2:3], heads, d, scale)
+    assert_close(f"one-round d{d}", one, ref, extra=_attn_extra(v[2:3], heads, d) + 1e-6)
+
+
 def test_attention_binding_rejects_bad_tensors_before_launch(V):
     heads, d, t, b = 2, 72, 65, 2
     w = heads * d

@@ -867,12 +867,241 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same attention for one-round grids (small batches): 16 queries per
+// wave with v_mfma_f32_16x16x32_f16, eight waves (128 queries) per
+// workgroup, two workgroups per CU. Per query it does the same products,
+// exponentials and rescales in the same order as flash_attn_vt_kernel, so
+// its outputs are bit-identical (tested); each wave's chain of dependent
+// steps per key block is half as long, which is what a grid of one round
+// waits on, while a full grid runs faster on the 32-query kernel, whose
+// waves read each K/V^T fragment once for twice the queries.
+//
+// K rows are stored permuted within each 32-key half: LDS row
+// 32h + 16t + 4g + i holds key 32h + 8g + 4t + i, so lane group g of score
+// tiles 2h and 2h + 1 (16x16 result: lane group g holds tile rows 4g..4g+3)
+// holds keys 32h + 8g .. 32h + 8g + 7, exactly the P^T operand of PV k-step
+// h. A K row has D/8 (made odd) 16-byte chunks: conflict-free fragment reads
+// of 16 consecutive rows; dims past D read the last real chunk, against zero
+// Q padding. V^T rows D (ones: the probability sum) .. 16 NT - 1 (zeros) are
+// written once.
+template <int D, bool OUT_FP8>
+__global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
+    const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
+    int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
+  static_assert(D % 8 == 0 && D >= 64 && D <= 80, "head width");
+  constexpr int NW = 8;
+  constexpr int QWG = NW * 16;
+  constexpr int NDC = D / 8;                       // 16-byte dim chunks of a key
+  constexpr int KP = 16 * (NDC | 1);               // K LDS row pitch (odd chunk count)
+  constexpr int KBYTES = KB * KP;
+  static_assert(KBYTES % 1024 == 0, "whole K transfers");
+  constexpr int NKS = (D + 31) / 32;               // QK k-steps of 32 dims
+  constexpr int NT = (D + 1 + 15) / 16;            // PV dim tiles: D dims and the ones row
+  constexpr int VR = 16 * NT;                      // V^T LDS rows
+  constexpr int STAGE = KBYTES + VR * VV_PITCH;
+  constexpr int NK = KBYTES / 1024;                // 1 KiB transfers for K per stage
+  constexpr int NDMA = NK + D / 8;                 // and for V^T (8 rows of 128 bytes each)
+  constexpr int PER_WAVE = (NDMA + NW - 1) / NW;
+  constexpr float kTau = 8.0f;                     // rescale only when a row max grows by > 2^8
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + 1024];
+  uint8_t* trash = smem + 2 * STAGE;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int fq = lane & 15;  // query of the wave (MFMA column)
+  const int g = lane >> 4;   // lane group
+  const int L = xcd_block(blockIdx.x, gridDim.x);
+  const int qb = L % nqb;
+  const int bh = L / nqb;
+  const int h = bh % H;
+  const int b = bh / H;
+  const int hc = h * D;
+  const int64_t img = (int64_t)b * T;
+  const int qi = qb * QWG + wave * 16 + fq;
+  const f16* vth = vt + (int64_t)bh * D * vt_ld;
+
+  // Q^T operand of k-step ks: dims 32 ks + 8 g .. + 7 of query qi (zero past D or T)
+  f16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int d0 = 32 * ks + 8 * g;
+    if (qi < T && d0 < D)
+      qf[ks] = *reinterpret_cast<const f16x8*>(q + (img + qi) * ld + hc + d0);
+    else
+      qf[ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // as in flash_attn_vt_kernel: Q complete before the block loop
+  constexpr int ZCH = (VR - D) * VV_PITCH / 16;
+  for (int i = t; i < 2 * ZCH; i += NW * 64) {
+    const int r = i % ZCH;
+    uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
+    const int one = 0x3C003C00;  // two F16 ones
+    *reinterpret_cast<i32x4*>(z) = r < VV_PITCH / 16 ? i32x4{one, one, one, one} : i32x4{0, 0, 0, 0};
+  }
+  __syncthreads();
+
+  // transfer slots (global index jg = wave + 8 j): K LDS bytes jg KiB .. (row off / KP, chunk),
+  // V^T rows 8 (jg - NK) .., padding transfers into the trash KiB
+  const f16* src[PER_WAVE];
+  int kkey[PER_WAVE], kdc[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int jg = wave + NW * j;
+    const int off = jg * 1024 + 16 * lane;
+    const int r = off / KP;
+    const int x = r & 31;
+    kkey[j] = (r & ~31) + 8 * ((x >> 2) & 3) + 4 * (x >> 4) + (x & 3);
+    kdc[j] = min((off % KP) / 16, NDC - 1);
+    if (jg < NK) {
+      src[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
+    } else if (jg < NDMA) {
+      const int d = 8 * (jg - NK) + (lane >> 3);
+      src[j] = vth + (int64_t)d * vt_ld + 8 * ((lane & 7) ^ vswz_key(d));
+    } else {
+      src[j] = vth;
+    }
+  }
+  auto issue = [&](int kb) {
+    const int key0 = kb * KB;
+    uint8_t* st = smem + (kb & 1) * STAGE;
+    const bool tail = key0 + KB > T;  // keys past T re-read token T-1
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int jg = wave + NW * j;
+      if (jg < NK) {
+        const f16* p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
+                            : src[j] + (int64_t)key0 * ld;
+        dma16(p, st + jg * 1024);
+      } else if (jg < NDMA) {
+        dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
+      } else {
+        dma16(src[j], trash);
+      }
+    }
+  };
+
+  int koff[NKS];  // K fragment: row fq of a tile, chunk 4 ks + g (the last real chunk past D)
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = fq * KP + min(4 * ks + g, NDC - 1) * 16;
+
+  float m_run = kNegInf;
+  f32x4 oacc[NT];  // O^T rows 16 dt + 4 g + (0..3), column fq
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nkb = (T + KB - 1) / KB;
+  issue(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();             // block kb in LDS; block kb-1's stage free
+    if (kb + 1 < nkb) issue(kb + 1);
+    const uint8_t* st = smem + (kb & 1) * STAGE;
+    const int key0 = kb * KB;
+    f32x4 sacc[4];  // S^T tile tt: LDS rows 16 tt + 4 g + i, query fq
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const f16x8 kf = *reinterpret_cast<const f16x8*>(st + tt * 16 * KP + koff[ks]);
+        sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], sacc[tt], 0, 0, 0);
+      }
+    }
+    if (key0 + KB > T) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + 32 * (tt >> 1) + 8 * g + 4 * (tt & 1) + i >= T) sacc[tt][i] = kNegInf;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
+                         fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
+    {  // over the four lane groups of query fq: lane rows 0/1 and 2/3, then the halves
+      unsigned a = __builtin_bit_cast(unsigned, mx), bb = a;
+      asm volatile("" : "+v"(bb));  // two distinct operands (see half_swap)
+      const auto sw = __builtin_amdgcn_permlane16_swap(a, bb, false, false);
+      const unsigned e0 = sw[0], e1 = sw[1];
+      mx = half_swap_max(fmaxf(__builtin_bit_cast(float, e0), __builtin_bit_cast(float, e1)));
+    }
+    // lazy running reference, as in flash_attn_vt_kernel
+    if (__any((mx - m_run) * c > kTau)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {  // PV k-step: keys 32 hh + 8 g .. + 7 of this lane group
+      f16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const int tt = 2 * hh + (e >> 2), i = e & 3;
+        const f32x2 pp = {__builtin_amdgcn_exp2f(fmaf(sacc[tt][i], c, -mc)),
+                          __builtin_amdgcn_exp2f(fmaf(sacc[tt][i + 1], c, -mc))};
+        const f16x2 ph = __builtin_convertvector(pp, f16x2);
+        pf[e] = ph[0];
+        pf[e + 1] = ph[1];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        const int vr = 16 * dt + fq;
+        const f16x8 vf =
+            *reinterpret_cast<const f16x8*>(st + KBYTES + vr * VV_PITCH + 16 * ((4 * hh + g) ^ vswz_key(vr)));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+  // the probability sum sits in O^T row D: tile D / 16, lane group (D % 16) / 4, register D % 4
+  const float lsum = __shfl(oacc[D / 16][D % 4], ((D % 16) / 4) * 16 + fq, 64);
+  if (qi >= T) return;
+  const float inv = 1.0f / lsum;
+#pragma unroll
+  for (int dt = 0; dt < NT; ++dt) {
+    const int d0 = 16 * dt + 4 * g;
+    if (d0 >= D) continue;
+    const float a0 = oacc[dt][0] * inv, a1 = oacc[dt][1] * inv, a2 = oacc[dt][2] * inv, a3 = oacc[dt][3] * inv;
+    if constexpr (OUT_FP8) {
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(o) + (img + qi) * ldo + hc + d0) =
+          pack4_e4m3(a0 * out_scale, a1 * out_scale, a2 * out_scale, a3 * out_scale);
+    } else {
+      const f16x4 ov = {(f16)a0, (f16)a1, (f16)a2, (f16)a3};
+      *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(o) + (img + qi) * ldo + hc + d0) = ov;
+    }
+  }
+}
+
 template <int D, bool QK8>
 hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o, int64_t ldo,
                        int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale, hipStream_t s) {
   const int nqb = (tokens + QB - 1) / QB;
   const int64_t blocks = (int64_t)nqb * heads * batch;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  // One round of workgroups (batch 1 and 2 at 729 tokens x 16 heads): the
+  // 16-query kernel, the same bits (729 tokens, 16 heads, head dim 72, batch
+  // 1 / 2: 20.2 -> 19.3 us, 21.5 -> 20.4 us; from batch 3 on the 32-query
+  // kernel is as fast or faster)
+  if constexpr (!QK8) {
+    if (blocks <= 256) {
+      const unsigned nb = (unsigned)((tokens + 127) / 128 * heads * batch);
+      const int nq16 = (tokens + 127) / 128;
+      const f16* q16 = static_cast<const f16*>(q);
+      const f16* k16 = static_cast<const f16*>(k);
+      if (out_fp8)
+        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld, o, ldo,
+                           tokens, heads, nq16, sl2, out_scale);
+      else
+        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, false>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld, o,
+                           ldo, tokens, heads, nq16, sl2, out_scale);
+      return hipGetLastError();
+    }
+  }
   if (out_fp8)
     hipLaunchKernelGGL((flash_attn_vt_kernel<D, true, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
                        dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
