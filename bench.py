@@ -234,7 +234,8 @@ def sweep(args):
     attention block (LN + QKV + attention + out-proj) and the MLP block
     (LN + up + down) from per-launch HIP events at B = 1 and B = 64; fused
     against separate Q/K/V projections; F16 against e4m3 attention products
-    (PV, QK, both)."""
+    (PV, QK, both); LayerNorms 1 and 2 as kernels against folded into the
+    QKV and MLP-up GEMMs (statistics kernel + normalizing GEMMs)."""
     import torch
 
     import synthetic as S
@@ -246,7 +247,7 @@ def sweep(args):
     del wt
     xall = torch.from_numpy(S.make_pixels(d, 64, 2)).cuda()
     res = {"workload": "SigLIP So400m/14 27 layers + MAP, synthetic seed-2 input and weights", "batches": {}, "blocks": {},
-           "qkv_projections": {}, "attention_products": {}}
+           "qkv_projections": {}, "attention_products": {}, "layernorm_fold": {}}
     batches = [1, 2, 4, 8, 16, 32, 64]
     for fp8 in (True, False):
         tag = "e4m3" if fp8 else "f16"
@@ -292,6 +293,23 @@ def sweep(args):
             res["attention_products"][tag][f"b{b}"] = {"ms": round(ms, 4), "images_per_s": round(b / ms * 1e3, 2),
                                                        "attention_us": round(ct["ATTENTION"][0], 2),
                                                        "qkv_us": round(ct["QKV"][0], 2)}
+        model.close()
+    for fold in (False, True):
+        model = V.Model(blob, max_batch=64, fp8=True, layernorm_fold=fold)
+        tag = "folded" if fold else "kernel"
+        res["layernorm_fold"][tag] = {}
+        for b in (1, 64):
+            x = xall[:b].contiguous()
+            out = torch.empty((b, 1, d.width), dtype=torch.float16, device="cuda")
+            ms = time_calls(model, x, out, args.sweep_steps if b > 1 else 4 * args.sweep_steps)
+            ct = class_times(model, x, out)
+            # LAYERNORM launches: the two per layer (statistics kernels when
+            # folded) plus the final and MAP LayerNorm kernels
+            ln_us = ct["LAYERNORM"][0] * ct["LAYERNORM"][1]
+            res["layernorm_fold"][tag][f"b{b}"] = {
+                "ms": round(ms, 4), "images_per_s": round(b / ms * 1e3, 2),
+                "layernorm_us_per_call": round(ln_us, 2), "qkv_us": round(ct["QKV"][0], 2),
+                "mlp_up_us": round(ct["MLP_UP"][0], 2)}
         model.close()
     print(json.dumps(res), flush=True)
 

@@ -88,6 +88,19 @@ typedef struct {
    * gemm_precision; needs head_dim 64, 72 or 80 (UNSUPPORTED otherwise).
    * fp8_scale_exp must then be in -8..8. */
   int32_t attention_fp8;
+  /* 0 = each layer's two LayerNorms write their normalized output (F16, or
+   * e4m3 in FP8 mode) for the next GEMM (the default). 1 = LayerNorms 1 and
+   * 2 are folded into the GEMMs that consume them (the QKV and MLP-up
+   * projections): a statistics kernel writes each row's mean and rstd, and
+   * those GEMMs normalize the F16 residual rows as they load them, with the
+   * LayerNorm's per-element arithmetic, so the results are bitwise those of
+   * the default (page "FP8 attention and resident image/embedding
+   * transfers", "Full 27-layer ViT": operands prepared by the kernels that
+   * use them rather than by separate passes). Slower on MI355X: every
+   * column tile normalizes its rows again. Needs width 1152 (UNSUPPORTED
+   * otherwise). The final and MAP LayerNorms are unchanged; the test
+   * build's LN1 and LN2 stage captures are not produced. */
+  int32_t layernorm_fold;
 } siglip_options;
 
 /*

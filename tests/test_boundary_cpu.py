@@ -167,6 +167,28 @@ def test_bad_attention_fp8_value(blob1):
         assert b"fp8_scale_exp" in lib.siglip_last_error()
 
 
+def test_bad_layernorm_fold_value(blob1):
+    lib = V.load_library()
+    out = ctypes.c_void_p()
+    for bad in (2, -1):
+        opt = V.siglip_options(0, 1, 0, -4, 0, 0, 0, bad)
+        st = lib.siglip_create(blob1, len(blob1), ctypes.byref(opt), ctypes.byref(out))
+        assert st == V.SIGLIP_E_INVALID_ARG and not out.value
+        assert b"layernorm_fold" in lib.siglip_last_error()
+
+
+def test_layernorm_fold_needs_width_1152_before_the_device():
+    # width 1280 (16 heads of 80) is otherwise supported
+    d = S.ModelDims(width=1280, heads=16, head_dim=80, depth=1, mlp=288, tokens=4)
+    blob = bytes(S.pack_blob(d, S.make_weights(d, 0)))
+    lib = V.load_library()
+    out = ctypes.c_void_p()
+    opt = V.siglip_options(0, 1, 0, -4, 0, 0, 0, 1)
+    st = lib.siglip_create(blob, len(blob), ctypes.byref(opt), ctypes.byref(out))
+    assert st == V.SIGLIP_E_UNSUPPORTED and not out.value
+    assert b"layernorm_fold" in lib.siglip_last_error()
+
+
 def test_unsupported_width_is_reported_before_the_device():
     d = S.small_dims(1)   # width 144: not a multiple of 128
     e = _create(bytes(S.pack_blob(d, S.make_weights(d, 0))))

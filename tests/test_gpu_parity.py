@@ -836,6 +836,94 @@ def test_separate_qkv_matches_fused_bitwise(V, fp8, attn_fp8):
         sep.close()
 
 
+@pytest.mark.parametrize("fp8,attn_fp8,separate", [(False, 0, False), (True, 0, False), (True, 3, False),
+                                                   (False, 0, True)],
+                         ids=["f16", "fp8", "fp8_e4m3_qk_pv", "f16_separate_qkv"])
+def test_layernorm_fold_matches_layernorm_kernel_bitwise(V, fp8, attn_fp8, separate):
+    """LayerNorms 1 and 2 folded into the QKV and MLP-up GEMMs (a statistics
+    kernel, then GEMMs that normalize the F16 residual rows as they load
+    them) against the LayerNorm kernel + GEMM: the per-element arithmetic is
+    the LayerNorm kernel's, so every later stage and the embeddings are
+    identical, at batch 2 (one-round grids) and batch 24 (full-grid tiles of
+    the default path), two layers, with the folded projection writing every
+    epilogue's outputs (Q/K/V^T, e4m3 Q/K slots and V^T, GELU e4m3 codes)."""
+    dims = S.SO400M.with_depth(2)
+    wt = S.make_weights(dims, 5)
+    blob = S.pack_blob(dims, wt)
+    del wt
+    for b in (2, 24):
+        _flush(f"layernorm fold vs kernel, fp8={fp8}, attention_fp8={attn_fp8}, separate_qkv={separate}, B={b}")
+        x = torch.from_numpy(S.make_pixels(dims, b, 5)).cuda()
+        kw = dict(max_batch=b, fp8=fp8, attention_fp8=attn_fp8, separate_qkv=separate)
+        base = V.Model(blob, **kw)
+        fold = V.Model(blob, layernorm_fold=True, **kw)
+        base.debug_capture(1)
+        fold.debug_capture(1)
+        y0 = base.encode(x)
+        y1 = fold.encode(x)
+        torch.cuda.synchronize()
+        assert np.isfinite(y0.cpu().numpy()).all()
+        np.testing.assert_array_equal(y1.cpu().numpy().view(np.uint16), y0.cpu().numpy().view(np.uint16))
+        for st in ("QKV", "V_T", "ATTN", "H_ATTN", "MLP_HIDDEN", "H_OUT", "FINAL_LN"):
+            np.testing.assert_array_equal(fold.debug_stage(st).view(np.uint8), base.debug_stage(st).view(np.uint8))
+        base.close()
+        fold.close()
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
+def test_c0_layernorm_fold_end_to_end(V, fp8):
+    """c0 with LayerNorms 1 and 2 folded into the QKV and MLP-up GEMMs,
+    against the oracle: the folded projections' outputs (Q, K, V^T and the
+    GELU activations) against the oracle's LayerNorm and projection of the
+    GPU's own residual stage, and the embedding end to end."""
+    cfg = S.CONFIGS["c0_1layer_b1_f16"]
+    dims = S.SO400M.with_depth(1)
+    _flush(f"c0 layernorm fold fp8={fp8}")
+    model, wt = make_model(V, dims, cfg["seed"], max_batch=1, fp8=fp8, layernorm_fold=True)
+    model.debug_capture(0)
+    x = S.make_pixels(dims, 1, cfg["seed"])
+    y = run(model, x)
+    se = model.fp8_scale_exp
+    f = lambda n: _dec(model, model.debug_stage(n), fp8)
+    W, D, H, T = dims.width, dims.head_dim, dims.heads, dims.tokens
+    f64 = lambda n: wt[n].astype(np.float64)
+    # the folded operand: LayerNorm of the residual rounded to the operand
+    # type; where the GPU's F32 LayerNorm lands on the other side of a
+    # rounding midpoint the operand differs by one step, so the band adds one
+    # operand step per product term
+    def folded(h, p):
+        a = O.layer_norm(h, f64(p + ".g"), f64(p + ".b"))
+        if fp8:
+            a_op = O.fp8_operand(a, se)
+            step = 2.0 ** -3 * np.abs(a) + 2.0 ** (se - 9)   # e4m3 spacing (3 mantissa bits, subnormals)
+        else:
+            a_op = a.astype(np.float16).astype(np.float64)
+            step = ulp16(a)
+        return a_op, step
+    a1, s1 = folded(f("EMBED"), "layer0.ln1")
+    w = device_weight(wt, "layer0.qkv.w", fp8, se)
+    ref = O.linear(a1, w, f64("layer0.qkv.b"))
+    band = acc_tol(a1, w) + s1 @ np.abs(w) + 1e-6
+    assert_close("QKV (Q, K) from the folded LayerNorm", f("QKV"), ref[:, :2 * W], extra=band[:, :2 * W])
+    vt = model.debug_stage("V_T", full=True)[:, :T].reshape(H, D, T).transpose(2, 0, 1).reshape(T, W)
+    assert_close("V (from V^T) from the folded LayerNorm", vt, ref[:, 2 * W:], extra=band[:, 2 * W:])
+    a2, s2 = folded(f("H_ATTN"), "layer0.ln2")
+    w = device_weight(wt, "layer0.mlp1.w", fp8, se)
+    ref = O.gelu_tanh(O.linear(a2, w, f64("layer0.mlp1.b")))
+    band = 1.2 * (acc_tol(a2, w) + s2 @ np.abs(w)) + 1e-6
+    if fp8:
+        e4m3_within("MLP_HIDDEN from the folded LayerNorm", model.debug_stage("MLP_HIDDEN"), ref, se, band=band)
+    else:
+        assert_close("MLP_HIDDEN from the folded LayerNorm", f("MLP_HIDDEN"), ref, extra=band)
+    ref = O.encode(wt, x, dims.heads)
+    cos, mx = per_image_metrics(y, ref)
+    _flush(f"  c0 layernorm fold end-to-end fp8={fp8}: cosine {cos.min():.6f}, max abs {mx.max():.4e}")
+    if not fp8:
+        assert cos.min() >= 0.999 and mx.max() <= 2e-2
+    else:
+        assert cos.min() >= 0.99 and mx.max() <= 0.5
+
+
 def test_four_token_full_width_diagnostic(V):
     dims = S.four_token_dims(2)
     _flush("four-token diagnostic")

@@ -49,7 +49,7 @@ class siglip_options(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("gemm_precision", ctypes.c_int32), ("fp8_scale_exp", ctypes.c_int32),
                 ("separate_qkv", ctypes.c_int32), ("map_explicit_kv", ctypes.c_int32),
-                ("attention_fp8", ctypes.c_int32)]
+                ("attention_fp8", ctypes.c_int32), ("layernorm_fold", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -148,14 +148,15 @@ class Model:
 
     def __init__(self, blob, layers: int = 0, max_batch: int = 1, fp8: bool = False,
                  fp8_scale_exp: int = -4, separate_qkv: bool = False, map_explicit_kv: bool = False,
-                 attention_fp8=0):
+                 attention_fp8=0, layernorm_fold: bool = False):
         """attention_fp8: e4m3 attention products, siglip_options bits (1 = PV,
-        2 = QK, 3 = both); True means PV."""
+        2 = QK, 3 = both); True means PV. layernorm_fold: LayerNorms 1 and 2
+        folded into the QKV and MLP-up GEMMs (width 1152 only)."""
         lib = load_library()
         keep, ptr, n = _host_ptr(blob)
         afp8 = 1 if attention_fp8 is True else int(attention_fp8)
         opt = siglip_options(layers, max_batch, 1 if fp8 else 0, fp8_scale_exp, 1 if separate_qkv else 0,
-                             1 if map_explicit_kv else 0, afp8)
+                             1 if map_explicit_kv else 0, afp8, 1 if layernorm_fold else 0)
         h = ctypes.c_void_p()
         _check(lib.siglip_create(ptr, n, ctypes.byref(opt), ctypes.byref(h)))
         self._h = h

@@ -130,6 +130,12 @@ struct GemmArgs {
   // heads) is written as the e4m3 code of value*qk8_scale at byte
   // qk8 + m*qk8_ld + (n / vt_dim)*qk8_pitch + n % vt_dim
   uint8_t* qk8; int64_t qk8_ld; int qk8_pitch; float qk8_scale;
+  // LayerNorm folded into the A operand (ln_stats != nullptr): a is the F16
+  // residual [M, K] (lda in elements) and row m is normalized on its way into
+  // LDS as fma((x - mean) * rs, ln_gamma[k], ln_beta[k] * ln_scale), with
+  // {mean, rs} the two floats at ln_stats + 2m (launch_layernorm_stats), then
+  // rounded to the operand type.
+  const float* ln_stats; const float* ln_gamma; const float* ln_beta; float ln_scale;
 };
 
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8,
@@ -140,6 +146,13 @@ hipError_t launch_layernorm(const f16* x, int64_t ldx, void* y, int64_t ldy,
                             const float* gamma, const float* beta, int rows,
                             int width, float eps, bool out_fp8, float out_scale,
                             hipStream_t s);
+
+// Row statistics of the LayerNorm above for width 1152 only: {mean, rstd *
+// scale} per row as two floats at stats + 2 row, the values
+// launch_layernorm computes for the same row (hipErrorInvalidValue for
+// another width).
+hipError_t launch_layernorm_stats(const f16* x, int64_t ldx, float* stats, int rows, int width, float eps,
+                                  float scale, hipStream_t s);
 
 // ------------------------------------------------------------- attention
 hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v,

@@ -14,7 +14,14 @@
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales; the power-of-two
 // operand scale is folded into acc_scale). F32 accumulation.
 //
-// Tiling: a workgroup of 4 or 8 waves owns a BM x BN output tile and walks K in
+// LayerNorm-folded A operand (an option): A is the F16 residual stream and
+// each row is normalized with its precomputed statistics on its way into LDS
+// (page "FP8 attention and resident image/embedding transfers", "Full
+// 27-layer ViT": producers and consumers handle the quantized operand
+// themselves instead of separate passes), the per-element arithmetic of the
+// LayerNorm kernel, so the products are those of LayerNorm + GEMM.
+//
+// Tiling: a workgroup of 4 to 12 waves owns a BM x BN output tile and walks K in
 // 128-byte slices (64 F16 or 128 e4m3 values per row; 64-byte slices for the
 // MLP-up tile, 256-byte slices for one-round small grids with a long K).
 // Slices go global -> LDS directly (global_load_lds_dwordx4) into a ring of
@@ -125,8 +132,11 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
 
 // MINW: workgroups per CU the register allocation must allow (2 for the tile
 // that relies on two workgroups sharing a CU).
+// LNA: the A operand is LayerNorm-folded (GemmArgs::ln_stats): A rows are
+// the F16 residual, normalized in registers and written to LDS as operand
+// values; only the weight rows stream by DMA.
 template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8, int RB = kRowBytes,
-          int MINW = 1>
+          int MINW = 1, bool LNA = false>
 __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(GemmArgs g) {
   using T = Tile<BM, BN, WM, WN, RB>;
   static_assert(STAGES >= 2, "at least double buffering");
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
     const int row = R * j + T::RPW * wave + rr;
     if (R * j < BM) {
       const int am = min(m0 + row, g.M - 1);  // rows past M re-read row M-1; never stored
-      src[j] = reinterpret_cast<const uint8_t*>(g.a) + (int64_t)am * g.lda * E + lchunk * 16;
+      src[j] = LNA ? nullptr : reinterpret_cast<const uint8_t*>(g.a) + (int64_t)am * g.lda * E + lchunk * 16;
     } else {
       src[j] = reinterpret_cast<const uint8_t*>(g.w) + (int64_t)(n0 + row - BM) * g.ldw * E + lchunk * 16;
     }
@@ -171,7 +181,78 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % STAGES) * T::STAGE + T::RPW * wave * RB;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) dma16(src[j] + kt * RB, st + R * j * RB);
+    for (int j = 0; j < CH; ++j) {
+      if (LNA && R * j < BM) continue;  // the A rows are written by anorm
+      dma16(src[j] + kt * RB, st + R * j * RB);
+    }
+  };
+
+  // ---- LayerNorm-folded A operand. Each thread normalizes, per slice, NA
+  // chunks of 8 K-values: chunk column lcol of tile rows (t + i THREADS) /
+  // CPRA. The residual chunks, gamma and beta of slice kt + 1 are loaded
+  // while slice kt is multiplied. Per element the arithmetic is that of the
+  // LayerNorm kernel (fma((x - mean) rs, gamma, beta scale), then the
+  // operand rounding), so the LDS tile holds exactly what the LayerNorm
+  // kernel would have written.
+  constexpr int KV = RB / E;                            // K values per slice
+  constexpr int CPRA = KV / 8;                          // 8-value chunks per A row and slice
+  constexpr int NA = LNA ? BM * CPRA / T::THREADS : 1;  // chunks per thread and slice
+  static_assert(!LNA || (STAGES == 2 && (BM * CPRA) % T::THREADS == 0 && T::THREADS % CPRA == 0),
+                "LayerNorm-folded operand: two stages, whole chunks per thread");
+  const int lcol = t % CPRA;
+  const f16* asrc[NA];
+  float amean[NA], ars[NA];
+  f16x8 areg[NA];
+  f32x4 lgam[2], lbet[2];
+  if constexpr (LNA) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int am = min(m0 + (t + i * T::THREADS) / CPRA, g.M - 1);  // rows past M: never stored
+      const float2 st = reinterpret_cast<const float2*>(g.ln_stats)[am];
+      amean[i] = st.x;
+      ars[i] = st.y;
+      asrc[i] = reinterpret_cast<const f16*>(g.a) + (int64_t)am * g.lda + lcol * 8;
+    }
+  }
+  auto aload = [&](int kt) {
+    if constexpr (LNA) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) areg[i] = *reinterpret_cast<const f16x8*>(asrc[i] + kt * KV);
+      const int k0 = kt * KV + lcol * 8;
+      lgam[0] = *reinterpret_cast<const f32x4*>(g.ln_gamma + k0);
+      lgam[1] = *reinterpret_cast<const f32x4*>(g.ln_gamma + k0 + 4);
+      lbet[0] = *reinterpret_cast<const f32x4*>(g.ln_beta + k0);
+      lbet[1] = *reinterpret_cast<const f32x4*>(g.ln_beta + k0 + 4);
+    }
+  };
+  auto anorm = [&](int kt) {
+    if constexpr (LNA) {
+      uint8_t* st = smem + (kt % STAGES) * T::STAGE;
+      float gm[8], bt[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gm[e] = lgam[0][e];
+        gm[e + 4] = lgam[1][e];
+        bt[e] = lbet[0][e] * g.ln_scale;
+        bt[e + 4] = lbet[1][e] * g.ln_scale;
+      }
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int r = (t + i * T::THREADS) / CPRA;
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = fmaf(((float)areg[i][e] - amean[i]) * ars[i], gm[e], bt[e]);
+        if constexpr (FP8) {  // 8 codes: half of 16-byte chunk lcol / 2
+          *reinterpret_cast<uint2*>(st + r * RB + swz<RB>(r, lcol >> 1) * 16 + (lcol & 1) * 8) =
+              make_uint2(pack4_e4m3(o[0], o[1], o[2], o[3]), pack4_e4m3(o[4], o[5], o[6], o[7]));
+        } else {  // 8 F16 values: chunk lcol
+          f16x8 ov;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ov[e] = (f16)o[e];
+          *reinterpret_cast<f16x8*>(st + r * RB + swz<RB>(r, lcol) * 16) = ov;
+        }
+      }
+    }
   };
 
   f32x16 acc[T::TM][T::TN];
@@ -277,21 +358,41 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
     }
   }
 
-  // prologue: the first STAGES-1 slices in flight
-#pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nk) issue(p);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this thread's transfers of slice kt are done when at most the newer
-    // slices' transfers remain; the barrier then makes every wave's visible
-    // and guarantees that slice kt-1's buffer is no longer being read
-    if (kt + STAGES - 2 < nk)
-      wait_vmcnt<(STAGES - 2) * CH>();
-    else
+  if constexpr (LNA) {
+    // Two stages. Iteration kt writes the A part of stage kt % 2, last read
+    // by slice kt - 2's products, which every wave finished before the
+    // previous barrier; the barrier here makes the A rows and the weight
+    // transfers of slice kt visible, and slice kt - 1's stage free for the
+    // transfers of slice kt + 1.
+    aload(0);
+    issue(0);
+    for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-    compute(kt % STAGES);
+      anorm(kt);
+      __syncthreads();
+      if (kt + 1 < nk) {
+        aload(kt + 1);
+        issue(kt + 1);
+      }
+      compute(kt % STAGES);
+    }
+  } else {
+    // prologue: the first STAGES-1 slices in flight
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < nk) issue(p);
+    for (int kt = 0; kt < nk; ++kt) {
+      // this thread's transfers of slice kt are done when at most the newer
+      // slices' transfers remain; the barrier then makes every wave's visible
+      // and guarantees that slice kt-1's buffer is no longer being read
+      if (kt + STAGES - 2 < nk)
+        wait_vmcnt<(STAGES - 2) * CH>();
+      else
+        wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      compute(kt % STAGES);
+    }
   }
 
   // ---- epilogue: lane holds row m = tile row + fr, columns 8q + 4fg + (0..3)
@@ -464,11 +565,11 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool FP8, int EPI, bool OUT_FP8, int RB = kRowBytes,
-          int MINW = 1>
+          int MINW = 1, bool LNA = false>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   if (g.N % BN != 0 || (g.K * (FP8 ? 1 : 2)) % RB != 0) return hipErrorInvalidValue;  // whole tiles and slices
   dim3 grid((g.N / BN) * ((g.M + BM - 1) / BM));
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, FP8, EPI, OUT_FP8, RB, MINW>), grid,
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, FP8, EPI, OUT_FP8, RB, MINW, LNA>), grid,
                      dim3(Tile<BM, BN, WM, WN, RB>::THREADS), 0, s, g);
   return hipGetLastError();
 }
@@ -482,6 +583,18 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // with two LDS stages, two workgroups per CU. Small M falls back to
   // smaller tiles that still fill the 256 CUs.
   const long tiles_128 = (long)((g.M + 127) / 128) * (g.N / 128);
+  // LayerNorm-folded A operand (the epilogues of the projections that
+  // follow a LayerNorm): one tile shape at every size, 128x128 of eight
+  // waves, two stages
+  if constexpr (EPI == EPI_BIAS || EPI == EPI_QKV || EPI == EPI_QKV8 || EPI == EPI_BIAS_GELU) {
+    if (g.ln_stats) {
+      GemmArgs b = g;
+      if (b.group_m == 0 && tiles_128 >= 1024) b.group_m = 8;
+      return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8, kRowBytes, 1, true>(b, s);
+    }
+  } else {
+    if (g.ln_stats) return hipErrorInvalidValue;
+  }
   if (tiles_128 >= 1024) {
     // Large grids walk tiles in bands of row blocks (tile_of) unless the
     // caller chose a band: 4 row blocks for 256x256 tiles, 8 for the others
@@ -579,10 +692,14 @@ hipError_t launch_epi(const GemmArgs& g, int epi, bool out_fp8, hipStream_t s) {
 hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hipStream_t s) {
   // shape contract (checked here so no launch can index out of bounds)
   const int E = in_fp8 ? 1 : 2;
+  const int EA = g.ln_stats ? 2 : E;  // a LayerNorm-folded A operand is the F16 residual
   if (g.M < 1 || g.N < 64 || g.N % 128 != 0 || g.K < 1 || (g.K * E) % kRowBytes != 0)
     return hipErrorInvalidValue;
   if (g.lda < g.K || g.ldw < g.K || g.ldc < g.N) return hipErrorInvalidValue;
-  if ((int64_t)g.M * g.lda * E >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
+  if ((int64_t)g.M * g.lda * EA >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
+    return hipErrorInvalidValue;
+  if (g.ln_stats && (!g.ln_gamma || !g.ln_beta || (reinterpret_cast<uintptr_t>(g.ln_stats) & 7) ||
+                     (reinterpret_cast<uintptr_t>(g.ln_gamma) & 15) || (reinterpret_cast<uintptr_t>(g.ln_beta) & 15)))
     return hipErrorInvalidValue;
   // e4m3 output: the GELU epilogue's output, or V^T of the QKV epilogue
   const bool qkv = epi == EPI_QKV || epi == EPI_QKV8;
@@ -590,7 +707,7 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   // 16-byte transfers: operand rows, output rows and residual rows aligned
   const int OB = (out_fp8 && !qkv) ? 1 : 2;
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
-  if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * E) % 16 || (g.ldw * E) % 16 ||
+  if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * EA) % 16 || (g.ldw * E) % 16 ||
       (g.ldc * OB) % 16)
     return hipErrorInvalidValue;
   if (epi == EPI_BIAS_RES && (!g.res || misaligned(g.res) || g.ldres % 8 || g.ldres < g.N))

@@ -119,6 +119,13 @@ __device__ __forceinline__ float wave_sum_lanes(float v) {
   return lo + hi;
 }
 
+// a * b rounded to F32 on its own: the product is never fused with the
+// operation that consumes it
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // The same LayerNorm for a compile-time width WIDTH = 512 NF + 64 TW, with
 // waves that stay resident and walk rows r, r + (waves in the grid), ....
 // Every lane holds 8 NF + TW values of a row: NF 16-byte chunks (chunk
@@ -128,8 +135,16 @@ __device__ __forceinline__ float wave_sum_lanes(float v) {
 // flight while the current row is reduced and written. The centred values
 // are kept for the output, and the power-of-two e4m3 scale is applied to
 // rstd and beta (exact), so y = fma((x - mean) rstd, gamma, beta) before
-// scaling, as in layernorm_kernel; the row sums run in another order.
-template <bool OUT_FP8, int WIDTH>
+// scaling, as in layernorm_kernel; the row sums run in another order. The
+// mean is rounded before the values are centred (not fused into the
+// subtraction), so x - mean can be recomputed from the stored mean.
+//
+// STATS: the same kernel writes only each row's statistics, {mean, rstd *
+// out_scale} as two floats at y + 8 row bytes, for a GEMM that normalizes
+// its A operand itself (gemm.hip, LayerNorm-folded operand): it computes
+// fma((x - mean) * rs, gamma, beta * out_scale) per element, the arithmetic
+// below, so its operand equals this kernel's output bit for bit.
+template <bool OUT_FP8, int WIDTH, bool STATS = false>
 __global__ __launch_bounds__(256) void layernorm_rows_kernel(
     const f16* __restrict__ x, int64_t ldx, void* __restrict__ y, int64_t ldy,
     const float* __restrict__ gamma, const float* __restrict__ beta, int rows, float eps, float out_scale) {
@@ -139,21 +154,23 @@ __global__ __launch_bounds__(256) void layernorm_rows_kernel(
   static_assert(WIDTH % 64 == 0 && (TW == 0 || TW == 2) && NF >= 1 && NF <= 3, "row width");
   const int lane = threadIdx.x & 63;
   const int stride = gridDim.x * 4;  // waves in the grid
-  const float sc = OUT_FP8 ? out_scale : 1.0f;
+  const float sc = (OUT_FP8 || STATS) ? out_scale : 1.0f;
   float gm[NV], bt[NV];
+  if constexpr (!STATS) {  // (the statistics kernel takes no gamma or beta)
 #pragma unroll
-  for (int i = 0; i < NF; ++i) {
-    const int c = lane + 64 * i;
+    for (int i = 0; i < NF; ++i) {
+      const int c = lane + 64 * i;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      gm[8 * i + e] = gamma[8 * c + e];
-      bt[8 * i + e] = beta[8 * c + e] * sc;
+      for (int e = 0; e < 8; ++e) {
+        gm[8 * i + e] = gamma[8 * c + e];
+        bt[8 * i + e] = beta[8 * c + e] * sc;
+      }
     }
-  }
 #pragma unroll
-  for (int e = 0; e < TW; ++e) {
-    gm[8 * NF + e] = gamma[512 * NF + TW * lane + e];
-    bt[8 * NF + e] = beta[512 * NF + TW * lane + e] * sc;
+    for (int e = 0; e < TW; ++e) {
+      gm[8 * NF + e] = gamma[512 * NF + TW * lane + e];
+      bt[8 * NF + e] = beta[512 * NF + TW * lane + e] * sc;
+    }
   }
   struct Raw {
     f16x8 f[NF];
@@ -177,7 +194,7 @@ __global__ __launch_bounds__(256) void layernorm_rows_kernel(
 #pragma unroll
     for (int k = 0; k < NV; ++k) s += v[k];
     const float inv_w = 1.0f / (float)WIDTH;
-    const float mean = wave_sum_lanes(s) * inv_w;
+    const float mean = mul_rn(wave_sum_lanes(s), inv_w);
     float cs = 0.0f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -186,6 +203,10 @@ __global__ __launch_bounds__(256) void layernorm_rows_kernel(
     }
     const float var = wave_sum_lanes(cs) * inv_w;
     const float rs = (1.0f / sqrtf(var + eps)) * sc;
+    if constexpr (STATS) {
+      if (lane == 0) reinterpret_cast<float2*>(y)[row] = make_float2(mean, rs);
+      return;
+    }
     float o[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) o[k] = fmaf(v[k] * rs, gm[k], bt[k]);
@@ -251,6 +272,16 @@ hipError_t launch_layernorm(const f16* x, int64_t ldx, void* y, int64_t ldy,
   } else {
     hipLaunchKernelGGL((layernorm_kernel<false, 0>), grid, dim3(256), 0, s, x, ldx, y, ldy, gamma, beta, rows, width, eps, out_scale);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_stats(const f16* x, int64_t ldx, float* stats, int rows, int width, float eps,
+                                  float scale, hipStream_t s) {
+  if (rows < 1 || width != 1152 || ldx < width || (ldx & 7) || !stats || (reinterpret_cast<uintptr_t>(stats) & 7))
+    return hipErrorInvalidValue;
+  const dim3 rgrid(std::min((rows + 3) / 4, kRowsGridMax));
+  hipLaunchKernelGGL((layernorm_rows_kernel<false, 1152, true>), rgrid, dim3(256), 0, s, x, ldx, stats, 0,
+                     nullptr, nullptr, rows, eps, scale);
   return hipGetLastError();
 }
 

@@ -140,6 +140,10 @@ struct siglip_model {
   Gemm mq, mkv, mout, mmlp1, mmlp2;
   Gemm mk, mv;  // the two column blocks of mkv (separate-projection option only)
   bool separate_qkv = false;
+  // LayerNorms 1 and 2 folded into the QKV and MLP-up GEMMs: a statistics
+  // kernel writes {mean, rstd * scale} per row and the GEMMs normalize the
+  // F16 residual rows themselves
+  bool ln_fold = false;
   // MAP head with the K/V projection folded: u_h = W_k,h q_h in two F16
   // parts, W_v transposed per head [width (h, d), width (k)] and b_v F32
   bool map_fold = false;
@@ -164,6 +168,7 @@ struct siglip_model {
   f16* vt = nullptr;    // [B*heads*head_dim, tokens_pad] (vt_path only)
   float* mscores = nullptr;  // [B, 16, tokens] F32 (map_fold only)
   float* zbar = nullptr;     // [B, 16, width] F32 (map_fold only)
+  float* lnst = nullptr;     // [M, 2] F32 LayerNorm row statistics (ln_fold only)
 
   // diagnostics
   int capture_layer = -1;
@@ -301,6 +306,7 @@ struct Acts {
   void* vt;  // F16, or e4m3 codes with the e4m3 PV product
   float* mscores;
   float* zbar;
+  float* lnst;
 };
 
 Acts acts_at(const siglip_model* m, int b0) {
@@ -321,11 +327,29 @@ Acts acts_at(const siglip_model* m, int b0) {
   A.vt = at(m->vt, (int64_t)b0 * W * m->tokens_pad * (m->attn_fp8 ? 1 : 2));
   A.mscores = m->mscores ? m->mscores + r0 * 16 : nullptr;
   A.zbar = m->zbar ? m->zbar + (int64_t)b0 * 16 * W : nullptr;
+  A.lnst = m->lnst ? m->lnst + r0 * 2 : nullptr;
   return A;
 }
 
+// A LayerNorm folded into a GEMM's A operand: the rows' statistics and the
+// LayerNorm's affine parameters (a is then the F16 residual)
+struct LnFold {
+  const float* stats;
+  const float* gamma;
+  const float* beta;
+  float scale;
+};
+
+void set_ln(GemmArgs& args, const LnFold* ln) {
+  if (!ln) return;
+  args.ln_stats = ln->stats;
+  args.ln_gamma = ln->gamma;
+  args.ln_beta = ln->beta;
+  args.ln_scale = ln->scale;
+}
+
 void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, void* c, int64_t ldc, int epi,
-          bool out_fp8, const f16* res, int64_t ldres, hipStream_t s) {
+          bool out_fp8, const f16* res, int64_t ldres, hipStream_t s, const LnFold* ln = nullptr) {
   GemmArgs args{};
   args.a = a;
   args.lda = lda;
@@ -344,6 +368,7 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
   args.K = g.k_pad;
   args.acc_scale = m->acc_scale;
   args.out_scale = m->op_scale;
+  set_ln(args, ln);
   hip_check(launch_gemm(args, epi, m->fp8, out_fp8, s), "gemm launch");
 }
 
@@ -352,7 +377,7 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
 // (written into c, or as e4m3 codes into head slots of the QKV buffer's bytes
 // from qk8 on when the QK product is e4m3).
 GemmArgs qkv_args(siglip_model* m, const Gemm& g, const void* a, f16* c, void* vt, int vt_col0, uint8_t* qk8,
-                  int M) {
+                  int M, const LnFold* ln) {
   GemmArgs args{};
   args.a = a;
   args.lda = m->width;
@@ -379,13 +404,15 @@ GemmArgs qkv_args(siglip_model* m, const Gemm& g, const void* a, f16* c, void* v
     args.qk8_pitch = kQK8SlotBytes;
     args.qk8_scale = m->attn_v_scale;
   }
+  set_ln(args, ln);
   return args;
 }
 
 // The fused QKV projection: Q and K row-major into qkv (or as e4m3 codes in
 // its bytes), V transposed per head into vt when the streaming attention is
 // used.
-void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* vt, int M, hipStream_t s) {
+void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* vt, int M, hipStream_t s,
+              const LnFold* ln) {
   const Gemm& g = Ly.qkv;
   const int W = m->width;
   uint8_t* qk8 = reinterpret_cast<uint8_t*>(qkv);
@@ -393,29 +420,29 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* v
     // Q and K into their columns of the fused row (or their e4m3 head slots);
     // V as its own projection, transposed per head (all its columns are V)
     if (m->attn_qk8) {
-      hip_check(launch_gemm(qkv_args(m, Ly.q, a, qkv, vt, W, qk8, M), EPI_QKV8, m->fp8, m->attn_fp8, s),
+      hip_check(launch_gemm(qkv_args(m, Ly.q, a, qkv, vt, W, qk8, M, ln), EPI_QKV8, m->fp8, m->attn_fp8, s),
                 "q gemm launch");
-      hip_check(launch_gemm(qkv_args(m, Ly.k, a, qkv + W, vt, W, qk8 + (int64_t)m->heads * kQK8SlotBytes, M),
+      hip_check(launch_gemm(qkv_args(m, Ly.k, a, qkv + W, vt, W, qk8 + (int64_t)m->heads * kQK8SlotBytes, M, ln),
                             EPI_QKV8, m->fp8, m->attn_fp8, s),
                 "k gemm launch");
     } else {
-      gemm(m, Ly.q, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
-      gemm(m, Ly.k, a, W, M, qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, Ly.q, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
+      gemm(m, Ly.k, a, W, M, qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
     }
     if (!m->vt_path) {
-      gemm(m, Ly.v, a, W, M, qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+      gemm(m, Ly.v, a, W, M, qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
       return;
     }
     // c is not written: every column goes to vt
-    hip_check(launch_gemm(qkv_args(m, Ly.v, a, qkv + 2 * W, vt, 0, nullptr, M), EPI_QKV, m->fp8, m->attn_fp8, s),
+    hip_check(launch_gemm(qkv_args(m, Ly.v, a, qkv + 2 * W, vt, 0, nullptr, M, ln), EPI_QKV, m->fp8, m->attn_fp8, s),
               "v gemm launch");
     return;
   }
   if (!m->vt_path) {
-    gemm(m, g, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s);
+    gemm(m, g, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
     return;
   }
-  GemmArgs args = qkv_args(m, g, a, qkv, vt, 2 * W, qk8, M);
+  GemmArgs args = qkv_args(m, g, a, qkv, vt, 2 * W, qk8, M, ln);
   // 3456-wide weight (4 MB e4m3, 8 MB F16) exceeds an XCD's L2 next to the
   // activations: walk tiles in bands of 8 row blocks (measured ~12% faster
   // at 46,656 rows than row-block-major order)
@@ -537,14 +564,23 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
   for (int i = 0; i < m->layers; ++i) {
     const Layer& Ly = m->L[i];
     const bool ci = cap && i == m->capture_layer;
+    // LayerNorm 1: its output operand, or (folded) the row statistics the
+    // QKV GEMM normalizes the residual rows with
+    const LnFold ln1{A.lnst, Ly.ln1_g, Ly.ln1_b, q8 ? m->op_scale : 1.0f};
     {
       LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-      hip_check(launch_layernorm(A.h, W, A.a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
+      if (m->ln_fold)
+        hip_check(launch_layernorm_stats(A.h, W, A.lnst, M, W, 1e-6f, ln1.scale, s), "ln1 statistics");
+      else
+        hip_check(launch_layernorm(A.h, W, A.a, W, Ly.ln1_g, Ly.ln1_b, M, W, 1e-6f, q8, m->op_scale, s), "ln1");
     }
-    if (ci) capture(m, SIGLIP_STAGE_LN1, A.a, cb(SIGLIP_STAGE_LN1), s);
+    if (ci && !m->ln_fold) capture(m, SIGLIP_STAGE_LN1, A.a, cb(SIGLIP_STAGE_LN1), s);
     {
       LaunchTimer lt(m, SIGLIP_K_QKV, s);
-      gemm_qkv(m, Ly, A.a, A.qkv, A.vt, M, s);
+      if (m->ln_fold)
+        gemm_qkv(m, Ly, A.h, A.qkv, A.vt, M, s, &ln1);
+      else
+        gemm_qkv(m, Ly, A.a, A.qkv, A.vt, M, s, nullptr);
     }
     if (ci) capture(m, SIGLIP_STAGE_QKV, A.qkv, cb(SIGLIP_STAGE_QKV), s);
     if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, A.vt, cb(SIGLIP_STAGE_V_T), s);
@@ -578,14 +614,21 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
       gemm(m, Ly.out, A.o, W, M, A.h, W, EPI_BIAS_RES, false, A.h, W, s);
     }
     if (ci) capture(m, SIGLIP_STAGE_H_ATTN, A.h, cb(SIGLIP_STAGE_H_ATTN), s);
+    const LnFold ln2{A.lnst, Ly.ln2_g, Ly.ln2_b, q8 ? m->op_scale : 1.0f};
     {
       LaunchTimer lt(m, SIGLIP_K_LAYERNORM, s);
-      hip_check(launch_layernorm(A.h, W, A.a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
+      if (m->ln_fold)
+        hip_check(launch_layernorm_stats(A.h, W, A.lnst, M, W, 1e-6f, ln2.scale, s), "ln2 statistics");
+      else
+        hip_check(launch_layernorm(A.h, W, A.a, W, Ly.ln2_g, Ly.ln2_b, M, W, 1e-6f, q8, m->op_scale, s), "ln2");
     }
-    if (ci) capture(m, SIGLIP_STAGE_LN2, A.a, cb(SIGLIP_STAGE_LN2), s);
+    if (ci && !m->ln_fold) capture(m, SIGLIP_STAGE_LN2, A.a, cb(SIGLIP_STAGE_LN2), s);
     {
       LaunchTimer lt(m, SIGLIP_K_MLP_UP, s);
-      gemm(m, Ly.mlp1, A.a, W, M, A.u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
+      if (m->ln_fold)
+        gemm(m, Ly.mlp1, A.h, W, M, A.u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s, &ln2);
+      else
+        gemm(m, Ly.mlp1, A.a, W, M, A.u, m->mlp_pad, EPI_BIAS_GELU, q8, nullptr, 0, s);
     }
     if (ci) capture(m, SIGLIP_STAGE_MLP_HIDDEN, A.u, cb(SIGLIP_STAGE_MLP_HIDDEN), s);
     {
@@ -732,6 +775,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_INVALID_ARG, "attention_fp8 must be 0..3 (bit 0: PV product, bit 1: QK product)");
   if (opt->attention_fp8 != 0 && (opt->fp8_scale_exp < -8 || opt->fp8_scale_exp > 8))
     return fail(SIGLIP_E_INVALID_ARG, "fp8_scale_exp must be in -8..8");
+  if (opt->layernorm_fold != 0 && opt->layernorm_fold != 1)
+    return fail(SIGLIP_E_INVALID_ARG, "layernorm_fold must be 0 or 1");
   if (blob_bytes < sizeof(BlobHeader)) return fail(SIGLIP_E_BAD_BLOB, "blob shorter than its 64-byte header");
   BlobHeader h;
   std::memcpy(&h, blob, sizeof h);
@@ -742,6 +787,8 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     return fail(SIGLIP_E_INVALID_ARG, "layers must be 0 (all) or 1..depth");
   st = check_supported(h, &why);
   if (st != SIGLIP_OK) return fail(st, why);
+  if (opt->layernorm_fold == 1 && h.width != 1152)
+    return fail(SIGLIP_E_UNSUPPORTED, "layernorm_fold needs width 1152 (the statistics kernel's row layout)");
 
   // Walk the whole blob once on the CPU before touching the GPU.
   const int W = (int)h.width, F = (int)h.mlp, T = (int)h.tokens, P = (int)h.patch_dim;
@@ -823,6 +870,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->vt_path = flash_attention_vt_supported(m->head_dim);
     m->tokens_pad = (int)round_up(T, 64);
     m->separate_qkv = opt->separate_qkv == 1;
+    m->ln_fold = opt->layernorm_fold == 1;
     m->attn_fp8 = (opt->attention_fp8 & 1) != 0;
     m->attn_qk8 = (opt->attention_fp8 & 2) != 0;
     if ((m->attn_fp8 || m->attn_qk8) && !m->vt_path) {
@@ -888,6 +936,7 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
         {(void**)&m->vt, m->vt_path ? B * W * m->tokens_pad * (m->attn_fp8 ? 1 : 2) : 0},
         {(void**)&m->mscores, m->map_fold ? M * 16 * 4 : 0},
         {(void**)&m->zbar, m->map_fold ? B * 16 * W * 4 : 0},
+        {(void**)&m->lnst, m->ln_fold ? M * 2 * 4 : 0},
     };
     size_t total = 0;
     for (auto& p : parts) total += (size_t)round_up(p.bytes, 256);
