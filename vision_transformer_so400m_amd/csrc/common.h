@@ -112,7 +112,9 @@ enum GemmEpi : int {
 
 struct GemmArgs {
   const void* a; int64_t lda;     // elements
-  const void* w; int64_t ldw;     // elements (row n of Wt)
+  // Wt [N, K] in 64-byte K panels: byte b of row n (b = k * element size) at
+  // ((b / 64) * ldw + n) * 64 + b % 64; ldw = rows per panel (>= N)
+  const void* w; int64_t ldw;
   void* c; int64_t ldc;           // elements of the output type
   const float* bias;              // [N]
   const float* pos; int pos_rows; int64_t ldpos;
@@ -216,8 +218,11 @@ hipError_t launch_pad_convert(const f16* x, int64_t ldx, void* y, int rows,
                               int cols, int cols_pad, bool out_fp8, float scale,
                               hipStream_t s);
 
-// F32 weight [K, N] -> Wt [N_pad, K_pad] (F16 or e4m3 codes of w*scale),
-// zero in the padding.
+// F32 weight [K, N] -> Wt [N_pad, K_pad] (F16 or e4m3 codes of w*scale,
+// zero in the padding) in 64-byte K panels: byte b of row n at
+// ((b / 64) * N_pad + n) * 64 + b % 64 (K_pad * element size a multiple of
+// 64), so that any 64-byte-aligned K slice of consecutive rows is one
+// contiguous run per panel.
 hipError_t launch_weight_transpose(const float* w, int K, int N, void* wt,
                                    int K_pad, int N_pad, bool out_fp8,
                                    float scale, hipStream_t s);

@@ -7,8 +7,9 @@
 //    diagnosis", "Padding, SRAM placement and paired transfers": padding is
 //    read by the products, so it must hold zeros, never stale data).
 //  * weight_transpose: create-time F32 [K, N] -> [N_pad, K_pad] F16 or e4m3,
-//    K-contiguous, zero padding; staged through LDS so both the F32 reads and
-//    the narrow writes are coalesced.
+//    K-contiguous in 64-byte K panels (panel p holds bytes 64p..64p+63 of
+//    every row, rows consecutive), zero padding; staged through LDS so both
+//    the F32 reads and the narrow writes are coalesced.
 //  * f32_convert: create-time F32 rows -> padded F16/e4m3 rows (the probe).
 //  * vt_transpose: V [batch, tokens, width] -> V^T per image ([b width + c]
 //    rows of tokens, zero past the last token), the layout the streaming
@@ -67,11 +68,11 @@ __global__ __launch_bounds__(256) void weight_transpose_kernel(const float* __re
     const int n = n0 + ty + j, k = k0 + tx;
     if (n < N_pad && k < K_pad) {
       const float v = tile[tx][ty + j] * scale;
-      if constexpr (OUT_FP8) {
+      if constexpr (OUT_FP8) {  // 64 codes per panel row
         const uint32_t c = cvt_pk_e4m3(v, 0.0f, 0u, false);
-        reinterpret_cast<uint8_t*>(wt)[(int64_t)n * K_pad + k] = (uint8_t)(c & 0xFF);
-      } else {
-        reinterpret_cast<f16*>(wt)[(int64_t)n * K_pad + k] = (f16)v;
+        reinterpret_cast<uint8_t*>(wt)[((int64_t)(k >> 6) * N_pad + n) * 64 + (k & 63)] = (uint8_t)(c & 0xFF);
+      } else {  // 32 F16 values per panel row
+        reinterpret_cast<f16*>(wt)[((int64_t)(k >> 5) * N_pad + n) * 32 + (k & 31)] = (f16)v;
       }
     }
   }
@@ -157,7 +158,7 @@ hipError_t launch_pad_convert(const f16* x, int64_t ldx, void* y, int rows, int 
 
 hipError_t launch_weight_transpose(const float* w, int K, int N, void* wt, int K_pad, int N_pad,
                                    bool out_fp8, float scale, hipStream_t s) {
-  if (K < 1 || N < 1 || K_pad < K || N_pad < N) return hipErrorInvalidValue;
+  if (K < 1 || N < 1 || K_pad < K || N_pad < N || (K_pad * (out_fp8 ? 1 : 2)) % 64) return hipErrorInvalidValue;
   dim3 grid((K_pad + 31) / 32, (N_pad + 31) / 32);
   if (out_fp8)
     hipLaunchKernelGGL(weight_transpose_kernel<true>, grid, dim3(256), 0, s, w, K, N, wt, K_pad, N_pad, scale);

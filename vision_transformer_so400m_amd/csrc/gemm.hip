@@ -9,7 +9,10 @@
 // with batch) are applied to the F32 accumulators before the single F16 (or
 // e4m3) rounding of the output.
 //
-// Operands: A [M, K] activations and Wt [N, K] weights, both K-contiguous, both
+// Operands: A [M, K] activations, K-contiguous rows, and Wt [N, K] weights,
+// K-contiguous in 64-byte K panels (consecutive rows of one 64-byte piece of
+// K are contiguous, so every K slice of a weight tile is one run of memory
+// per panel: 64-byte slices cost half-line row fetches otherwise); both
 // F16 (v_mfma_f32_32x32x16_f16) or both OCP e4m3 codes
 // (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales; the power-of-two
 // operand scale is folded into acc_scale). F32 accumulation.
@@ -175,7 +178,9 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
       const int am = min(m0 + row, g.M - 1);  // rows past M re-read row M-1; never stored
       src[j] = LNA ? nullptr : reinterpret_cast<const uint8_t*>(g.a) + (int64_t)am * g.lda * E + lchunk * 16;
     } else {
-      src[j] = reinterpret_cast<const uint8_t*>(g.w) + (int64_t)(n0 + row - BM) * g.ldw * E + lchunk * 16;
+      // weight rows in 64-byte K panels: chunk c of the slice lies in panel c / 4
+      src[j] = reinterpret_cast<const uint8_t*>(g.w) + ((int64_t)(lchunk >> 2) * g.ldw + n0 + row - BM) * 64 +
+               (lchunk & 3) * 16;
     }
   }
   auto issue = [&](int kt) {
@@ -183,7 +188,8 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       if (LNA && R * j < BM) continue;  // the A rows are written by anorm
-      dma16(src[j] + kt * RB, st + R * j * RB);
+      // a slice further: RB bytes along an A row, RB / 64 panels of the weight
+      dma16(src[j] + (R * j < BM ? (int64_t)kt * RB : (int64_t)kt * RB * g.ldw), st + R * j * RB);
     }
   };
 
@@ -695,8 +701,8 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   const int EA = g.ln_stats ? 2 : E;  // a LayerNorm-folded A operand is the F16 residual
   if (g.M < 1 || g.N < 64 || g.N % 128 != 0 || g.K < 1 || (g.K * E) % kRowBytes != 0)
     return hipErrorInvalidValue;
-  if (g.lda < g.K || g.ldw < g.K || g.ldc < g.N) return hipErrorInvalidValue;
-  if ((int64_t)g.M * g.lda * EA >= (int64_t)1 << 31 || (int64_t)g.N * g.ldw * E >= (int64_t)1 << 31)
+  if (g.lda < g.K || g.ldw < g.N || g.ldc < g.N) return hipErrorInvalidValue;
+  if ((int64_t)g.M * g.lda * EA >= (int64_t)1 << 31 || (int64_t)g.K * E * g.ldw >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   if (g.ln_stats && (!g.ln_gamma || !g.ln_beta || (reinterpret_cast<uintptr_t>(g.ln_stats) & 7) ||
                      (reinterpret_cast<uintptr_t>(g.ln_gamma) & 15) || (reinterpret_cast<uintptr_t>(g.ln_beta) & 15)))
@@ -707,7 +713,7 @@ hipError_t launch_gemm(const GemmArgs& g, int epi, bool in_fp8, bool out_fp8, hi
   // 16-byte transfers: operand rows, output rows and residual rows aligned
   const int OB = (out_fp8 && !qkv) ? 1 : 2;
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
-  if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * EA) % 16 || (g.ldw * E) % 16 ||
+  if (misaligned(g.a) || misaligned(g.w) || misaligned(g.c) || (g.lda * EA) % 16 ||
       (g.ldc * OB) % 16)
     return hipErrorInvalidValue;
   if (epi == EPI_BIAS_RES && (!g.res || misaligned(g.res) || g.ldres % 8 || g.ldres < g.N))

@@ -70,7 +70,7 @@ constexpr int kNAlign = 128;  // N padding: the widest GEMM column tile
 constexpr int kQK8SlotBytes = 80;  // e4m3 Q/K head slot: 16-byte aligned rows for the attention's transfers
 
 struct Gemm {
-  void* w = nullptr;      // [n_pad, k_pad] F16 or e4m3, K-contiguous
+  void* w = nullptr;      // [n_pad, k_pad] F16 or e4m3, K-contiguous in 64-byte K panels
   float* bias = nullptr;  // [n_pad]
   int k = 0, n = 0, k_pad = 0, n_pad = 0;
 };
@@ -354,7 +354,7 @@ void gemm(siglip_model* m, const Gemm& g, const void* a, int64_t lda, int M, voi
   args.a = a;
   args.lda = lda;
   args.w = g.w;
-  args.ldw = g.k_pad;
+  args.ldw = g.n_pad;  // rows per 64-byte K panel
   args.c = c;
   args.ldc = ldc;
   args.bias = g.bias;
@@ -382,7 +382,7 @@ GemmArgs qkv_args(siglip_model* m, const Gemm& g, const void* a, f16* c, void* v
   args.a = a;
   args.lda = m->width;
   args.w = g.w;
-  args.ldw = g.k_pad;
+  args.ldw = g.n_pad;  // rows per 64-byte K panel
   args.c = c;
   args.ldc = 3 * m->width;
   args.bias = g.bias;
