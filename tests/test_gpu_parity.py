@@ -536,7 +536,7 @@ def _band_rows(M):
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
 def test_b64_layer0_stages_on_sampled_row_blocks(V, fp8):
     """The batch-64 launch shapes (192x384 tiles for QKV and MLP-down,
-    256x128 for MLP-up, 128x128 for the out-projection, banded tile order,
+    128x256 for MLP-up, 128x128 for the out-projection, banded tile order,
     the V-transposing and residual epilogues) element by element on sampled
     row blocks, at one layer (stage capture runs the batch on one stream, so
     every launch covers all 46,656 rows)."""

@@ -609,14 +609,18 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     // 256x256 tiles: not for the residual epilogue (its F32 staged tile
     // would not fit the LDS ring) nor the V-transposing one (a tile must not
     // straddle the V column boundary)
-    // GELU epilogue (MLP up, N % 128 == 0): 256x128 tiles of four waves
-    // (128x64 each) with a 3-stage ring of 64-byte K slices, 72 KiB of LDS, so
-    // two workgroups share a CU and one's VALU-heavy epilogue (bias, GELU,
-    // e4m3) runs beside the other's MFMA main loop (measured at 46,656 x
-    // 4,352 x 1,152: 2-7% faster than one 256x256 workgroup per CU, the same
-    // bits; slower for the residual and QKV epilogues).
+    // GELU epilogue (MLP up): tiles of four waves with a 3-stage ring of
+    // 64-byte K slices, 72 KiB of LDS, so two workgroups share a CU and one's
+    // VALU-heavy epilogue (bias, GELU, e4m3) runs beside the other's MFMA
+    // main loop (measured at 46,656 x 4,352 x 1,152: 2-7% faster than one
+    // 256x256 workgroup per CU, the same bits; slower for the residual and
+    // QKV epilogues). With N % 256 == 0, 128x256 tiles (waves of 64x128): the
+    // larger share of each slice is weight rows, which the 64-byte K panels
+    // make contiguous, so the activation rows' half-line fetches weigh less
+    // (255-273 against 267-287 us on two boxes, the same bits); else 256x128.
     if constexpr (EPI == EPI_BIAS_GELU) {
       if (b.group_m == 0) b.group_m = 8;
+      if (g.N % 256 == 0) return launch_cfg<128, 256, 64, 128, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
       return launch_cfg<256, 128, 128, 64, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
     }
     // Long K (MLP down, K = 4352) or wide N (the fused QKV projection, 3456;
