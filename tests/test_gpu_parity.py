@@ -446,7 +446,8 @@ def check_stages_rows(model, wt, x, dims, fp8, batch, rows):
     """Layer-0 stages EMBED .. H_OUT on the token rows `rows` only, element
     by element against the oracle on the GPU's own inputs (as check_stages),
     for batches too large to recompute whole. Attention rows take the K and
-    V of their whole image from the GPU's QKV and V^T stages."""
+    V of their whole image from the GPU's QKV stage (and its V^T stage where
+    V is written transposed)."""
     se = model.fp8_scale_exp
     T, W, H, D, F = dims.tokens, dims.width, dims.heads, dims.head_dim, dims.mlp
     M = batch * T
@@ -488,16 +489,21 @@ def check_stages_rows(model, wt, x, dims, fp8, batch, rows):
     gemm_rows("EMBED", xin, "embed.w", "embed.b", add=f64("pos")[rows % T])
     ln1 = O.layer_norm(val("EMBED"), f64("layer0.ln1.g"), f64("layer0.ln1.b"))
     check("LN1", stage("LN1")[rows], ln1, 1e-5)
-    assert stage("QKV").shape[1] == 2 * W, "the streaming path writes Q and K row-major, V transposed"
-    gemm_rows("QKV", val("LN1"), "layer0.qkv.w", "layer0.qkv.b", cols=2 * W)
-    vt = model.debug_stage("V_T", full=True)
-    assert not vt[:, T:].view(np.uint8).any(), "V^T padding must be exact zeros"
-    # V of token row r = b T + t, column h D + d sits at V^T row b W + h D + d, column t
-    vt3 = vt[:, :T].reshape(batch, W, T)
-    v_rows = vt3[rows // T, :, rows % T].astype(np.float64)
-    wv = dw("layer0.qkv.w")[:, 2 * W:]
-    assert_close("V (from V^T)", v_rows, O.linear(val("LN1"), wv, f64("layer0.qkv.b")[2 * W:]),
-                 extra=acc_tol(val("LN1"), wv) + 1e-6)
+    qcols = stage("QKV").shape[1]
+    assert qcols in (2 * W, 3 * W)
+    gemm_rows("QKV", val("LN1"), "layer0.qkv.w", "layer0.qkv.b", cols=qcols)
+    if qcols == 2 * W:  # V transposed per head
+        vt = model.debug_stage("V_T", full=True)
+        assert not vt[:, T:].view(np.uint8).any(), "V^T padding must be exact zeros"
+        # V of token row r = b T + t, column h D + d sits at V^T row b W + h D + d, column t
+        vt3 = vt[:, :T].reshape(batch, W, T)
+        v_rows = vt3[rows // T, :, rows % T].astype(np.float64)
+        wv = dw("layer0.qkv.w")[:, 2 * W:]
+        assert_close("V (from V^T)", v_rows, O.linear(val("LN1"), wv, f64("layer0.qkv.b")[2 * W:]),
+                     extra=acc_tol(val("LN1"), wv) + 1e-6)
+        v_img = lambda b: vt3[b].T.astype(np.float64)
+    else:  # V row-major in the QKV rows (checked with them above)
+        v_img = lambda b: stage("QKV")[b * T:(b + 1) * T, 2 * W:].astype(np.float64)
     # attention of the sampled query rows against their image's keys
     ref_attn = np.empty((len(rows), W))
     band = np.empty((len(rows), W))
@@ -505,7 +511,7 @@ def check_stages_rows(model, wt, x, dims, fp8, batch, rows):
     for b in np.unique(rows // T):
         sel = np.nonzero(rows // T == b)[0]
         kk = qkv[b * T:(b + 1) * T, W:2 * W].astype(np.float64)
-        vv = vt3[b].T.astype(np.float64)
+        vv = v_img(b)
         qq = qkv[rows[sel], :W].astype(np.float64)
         o = _attn_ref(qq[None], kk[None], vv[None], H, D, 1 / math.sqrt(D))[0]
         ref_attn[sel] = o
@@ -904,9 +910,13 @@ def test_c0_layernorm_fold_end_to_end(V, fp8):
     w = device_weight(wt, "layer0.qkv.w", fp8, se)
     ref = O.linear(a1, w, f64("layer0.qkv.b"))
     band = acc_tol(a1, w) + s1 @ np.abs(w) + 1e-6
-    assert_close("QKV (Q, K) from the folded LayerNorm", f("QKV"), ref[:, :2 * W], extra=band[:, :2 * W])
-    vt = model.debug_stage("V_T", full=True)[:, :T].reshape(H, D, T).transpose(2, 0, 1).reshape(T, W)
-    assert_close("V (from V^T) from the folded LayerNorm", vt, ref[:, 2 * W:], extra=band[:, 2 * W:])
+    qkv = f("QKV")
+    if qkv.shape[1] == 2 * W:  # V transposed per head
+        v = model.debug_stage("V_T", full=True)[:, :T].reshape(H, D, T).transpose(2, 0, 1).reshape(T, W)
+    else:
+        qkv, v = qkv[:, :2 * W], qkv[:, 2 * W:]
+    assert_close("QKV (Q, K) from the folded LayerNorm", qkv, ref[:, :2 * W], extra=band[:, :2 * W])
+    assert_close("V from the folded LayerNorm", v, ref[:, 2 * W:], extra=band[:, 2 * W:])
     a2, s2 = folded(f("H_ATTN"), "layer0.ln2")
     w = device_weight(wt, "layer0.mlp1.w", fp8, se)
     ref = O.gelu_tanh(O.linear(a2, w, f64("layer0.mlp1.b")))

@@ -315,21 +315,62 @@ __device__ __forceinline__ void attn_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Row-major V (VROW). A stage's V part holds the block's 64 key rows, in key
+// order, kVRowPitch bytes each: dims 0..D-1 of the key, then the chunk
+// {1, 0, ..., 0} at dim D (the PV product then also yields each query's
+// probability sum) and zero chunks up to dim 95. The padding chunks are
+// written once per stage (vrow_pad); the transfer lanes that would land on
+// them are masked off.
+// Transposing LDS reads (ds_read_b64_tr_b16) give the PV A operand: within
+// each 16-lane group, lane a + 4r reads four dims of key k + r, and lane
+// 4a + b receives dim b of those four keys. With a 192-byte pitch, four
+// consecutive rows start in four distinct 64-byte bank ranges.
+constexpr int kVRowPitch = 192;
+constexpr int VR_BYTES = KB * kVRowPitch;  // 12 KiB
+
+// the padding chunks (NDC .. 11) of the 64 V rows of `stages` stages of
+// `stage_bytes` whose V part starts at vbase; threads t = 0 .. nthreads - 1
+template <int NDC>
+__device__ __forceinline__ void vrow_pad(uint8_t* smem, int stages, int stage_bytes, int vbase, int t, int nthreads) {
+  constexpr int PC = kVRowPitch / 16 - NDC;  // padding chunks per row
+  for (int i = t; i < stages * KB * PC; i += nthreads) {
+    const int c = i % PC, r = (i / PC) % KB, st = i / (PC * KB);
+    const int one = c == 0 ? 0x3C00 : 0;  // F16 1 in the first dim of the first padding chunk
+    *reinterpret_cast<i32x4*>(smem + st * stage_bytes + vbase + r * kVRowPitch + (NDC + c) * 16) =
+        i32x4{one, 0, 0, 0};
+  }
+}
+
+// four F16 of four consecutive rows (see above), as one half of an f16x8 operand
+__device__ __forceinline__ f16x4 ds_read_tr4(const uint8_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<uint8_t*>(p)));
+  return __builtin_bit_cast(f16x4, r);
+}
+__device__ __forceinline__ f16x8 cat8(f16x4 lo, f16x4 hi) {
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // QK8: q and k are e4m3 codes (head h of a token row at byte h * kQK8Pitch,
 // ld in bytes), their products scaled into c by the caller.
-template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1, bool QK8 = false>
+// VROW: vt is V row-major (rows of stride ld, head h at column h * D, as q
+// and k), read through the transposing LDS reads; vt_ld is not used.
+template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1, bool QK8 = false,
+          bool VROW = false>
 __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
   static_assert(!QK8 || QT == 1, "e4m3 Q/K with one query tile per wave");
+  static_assert(!VROW || (!QK8 && QT == 1), "row-major V with F16 Q/K, one query tile per wave");
   constexpr int QWG = 4 * 32 * QT;               // queries per workgroup
   constexpr int NDC = D / 8;                     // 16-byte dim chunks per key
   constexpr int KBYTES = QK8 ? VK8_BYTES : VK_BYTES;
-  constexpr int STAGE = KBYTES + VROWS * VV_PITCH;
+  constexpr int STAGE = KBYTES + (VROW ? VR_BYTES : VROWS * VV_PITCH);
   constexpr int NK = KBYTES / 1024;              // 1 KiB transfers for K per stage
-  constexpr int NDMA = NK + D / 8;               // 1 KiB transfers per stage
+  constexpr int NDMA = NK + (VROW ? VR_BYTES / 1024 : D / 8);  // 1 KiB transfers per stage
   constexpr int PER_WAVE = (NDMA + 3) / 4;       // every wave issues the same count
   constexpr int RL = (D - 64) / 2;               // oacc[.][2] register holding O^T row D (lane group 0)
   constexpr float kTau = 8.0f;                   // rescale only when a row max grows by > 2^8
@@ -384,7 +425,9 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   // constant V^T rows of every stage: row D = 1 (the PV product then also
   // yields each query's sum of the F16 probabilities it used), rows D+1..95 = 0
-  constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
+  // (row-major V brings its padding with every transfer)
+  if constexpr (VROW) vrow_pad<NDC>(smem, VT_STAGES, STAGE, KBYTES, t, 256);
+  constexpr int ZCH = VROW ? 0 : (VROWS - D) * VV_PITCH / 16;
   for (int i = t; i < VT_STAGES * ZCH; i += 256) {
     const int r = i % ZCH;
     uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
@@ -404,6 +447,13 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   for (int j = 0; j < PER_WAVE; ++j) {
     const int jg = wave + 4 * j;
     const int off = jg * 1024 + 16 * lane;
+    if (VROW && jg >= NK && jg < NDMA) {  // V row kkey, chunk kdc (>= NDC: padding, not transferred)
+      const int vo = off - NK * 1024;
+      kkey[j] = vo / kVRowPitch;
+      kdc[j] = (vo % kVRowPitch) / 16;
+      src[j] = vt + (img + kkey[j]) * ld + hc + 8 * min(kdc[j], NDC - 1);
+      continue;
+    }
     if constexpr (QK8) {  // K row of kQK8Pitch code bytes: 5 chunks of 16
       kkey[j] = key_of_row(off / kQK8Pitch);
       kdc[j] = (off % kQK8Pitch) / 16;
@@ -440,7 +490,13 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
                    : src[j] + (int64_t)key0 * ld;
         dma16(p, st + jg * 1024);
       } else if (jg < NDMA) {
-        dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
+        if constexpr (VROW) {
+          const f16* p = tail ? vt + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
+                              : src[j] + (int64_t)key0 * ld;
+          if (kdc[j] < NDC) dma16(p, st + jg * 1024);
+        } else {
+          dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
+        }
       } else {
         dma16(src[j], trash);
       }
@@ -452,6 +508,12 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   int voff[4];                                                   // + dt*32*128
 #pragma unroll
   for (int s = 0; s < 4; ++s) voff[s] = KBYTES + fr * VV_PITCH + 16 * ((2 * s + fg) ^ vswz_key(fr));
+  // VROW: lane a + 4r of 16-lane group G reads dims 16 (G & 1) + 4a .. + 3 of
+  // key 8 (G >> 1) + r (+ 16 s + 4 t for PV k-step s, half t; + 32 dt dims):
+  // lane 4a + b then holds dim 16 (G & 1) + 4a + b = fr of keys
+  // 16 s + 8 fg + 4 t + 0..3, the A operand of the 32x32x16 product
+  const int vrb = KBYTES + (8 * (lane >> 5) + ((lane & 15) >> 2)) * kVRowPitch +
+                  2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   float m_run[QT];
   f32x16 oacc[QT][3];
@@ -554,7 +616,13 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
         }
 #pragma unroll
       for (int dt = 0; dt < 3; ++dt) {  // keys 16s + 8fg + (0..7) of dim row 32dt + fr
-        const f16x8 vf = *reinterpret_cast<const f16x8*>(st + voff[s] + dt * 32 * VV_PITCH);
+        f16x8 vf;
+        if constexpr (VROW) {
+          const uint8_t* pv = st + vrb + 16 * s * kVRowPitch + 64 * dt;
+          vf = cat8(ds_read_tr4(pv), ds_read_tr4(pv + 4 * kVRowPitch));
+        } else {
+          vf = *reinterpret_cast<const f16x8*>(st + voff[s] + dt * 32 * VV_PITCH);
+        }
 #pragma unroll
         for (int u = 0; u < QT; ++u)
           oacc[u][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], oacc[u][dt], 0, 0, 0);
@@ -884,8 +952,8 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
 // h. A K row has D/8 (made odd) 16-byte chunks: conflict-free fragment reads
 // of 16 consecutive rows; dims past D read the last real chunk, against zero
 // Q padding. V^T rows D (ones: the probability sum) .. 16 NT - 1 (zeros) are
-// written once.
-template <int D, bool OUT_FP8>
+// written once. VROW: vt is V row-major, as for flash_attn_vt_kernel.
+template <int D, bool OUT_FP8, bool VROW = false>
 __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
     const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
@@ -899,9 +967,10 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
   constexpr int NKS = (D + 31) / 32;               // QK k-steps of 32 dims
   constexpr int NT = (D + 1 + 15) / 16;            // PV dim tiles: D dims and the ones row
   constexpr int VR = 16 * NT;                      // V^T LDS rows
-  constexpr int STAGE = KBYTES + VR * VV_PITCH;
+  static_assert(!VROW || VR <= kVRowPitch / 2, "row-major V rows hold the PV dim tiles");
+  constexpr int STAGE = KBYTES + (VROW ? VR_BYTES : VR * VV_PITCH);
   constexpr int NK = KBYTES / 1024;                // 1 KiB transfers for K per stage
-  constexpr int NDMA = NK + D / 8;                 // and for V^T (8 rows of 128 bytes each)
+  constexpr int NDMA = NK + (VROW ? VR_BYTES / 1024 : D / 8);  // and for V (V^T: 8 rows of 128 bytes each)
   constexpr int PER_WAVE = (NDMA + NW - 1) / NW;
   constexpr float kTau = 8.0f;                     // rescale only when a row max grows by > 2^8
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + 1024];
@@ -933,7 +1002,8 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
       qf[ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   __builtin_amdgcn_s_waitcnt(0);  // as in flash_attn_vt_kernel: Q complete before the block loop
-  constexpr int ZCH = (VR - D) * VV_PITCH / 16;
+  if constexpr (VROW) vrow_pad<NDC>(smem, 2, STAGE, KBYTES, t, NW * 64);
+  constexpr int ZCH = VROW ? 0 : (VR - D) * VV_PITCH / 16;
   for (int i = t; i < 2 * ZCH; i += NW * 64) {
     const int r = i % ZCH;
     uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
@@ -954,7 +1024,12 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
     const int x = r & 31;
     kkey[j] = (r & ~31) + 8 * ((x >> 2) & 3) + 4 * (x >> 4) + (x & 3);
     kdc[j] = min((off % KP) / 16, NDC - 1);
-    if (jg < NK) {
+    if (VROW && jg >= NK && jg < NDMA) {  // V row kkey, chunk kdc (>= NDC: padding, not transferred)
+      const int vo = off - NK * 1024;
+      kkey[j] = vo / kVRowPitch;
+      kdc[j] = (vo % kVRowPitch) / 16;
+      src[j] = vt + (img + kkey[j]) * ld + hc + 8 * min(kdc[j], NDC - 1);
+    } else if (jg < NK) {
       src[j] = k + (img + kkey[j]) * ld + hc + 8 * kdc[j];
     } else if (jg < NDMA) {
       const int d = 8 * (jg - NK) + (lane >> 3);
@@ -975,12 +1050,22 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
                             : src[j] + (int64_t)key0 * ld;
         dma16(p, st + jg * 1024);
       } else if (jg < NDMA) {
-        dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
+        if constexpr (VROW) {
+          const f16* p = tail ? vt + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
+                              : src[j] + (int64_t)key0 * ld;
+          if (kdc[j] < NDC) dma16(p, st + jg * 1024);
+        } else {
+          dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
+        }
       } else {
         dma16(src[j], trash);
       }
     }
   };
+  // VROW: lane a + 4r of lane group g reads dims 4a .. 4a + 3 of key 8g + r
+  // (+ 32 hh + 4 t for PV k-step hh, half t; + 16 dt dims): lane 4a + b then
+  // holds dim fq of keys 32 hh + 8 g + 4 t + 0..3
+  const int vrb = KBYTES + (8 * g + ((lane & 15) >> 2)) * kVRowPitch + 8 * (lane & 3);
 
   int koff[NKS];  // K fragment: row fq of a tile, chunk 4 ks + g (the last real chunk past D)
 #pragma unroll
@@ -1051,9 +1136,14 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
       }
 #pragma unroll
       for (int dt = 0; dt < NT; ++dt) {
-        const int vr = 16 * dt + fq;
-        const f16x8 vf =
-            *reinterpret_cast<const f16x8*>(st + KBYTES + vr * VV_PITCH + 16 * ((4 * hh + g) ^ vswz_key(vr)));
+        f16x8 vf;
+        if constexpr (VROW) {
+          const uint8_t* pv = st + vrb + 32 * hh * kVRowPitch + 32 * dt;
+          vf = cat8(ds_read_tr4(pv), ds_read_tr4(pv + 4 * kVRowPitch));
+        } else {
+          const int vr = 16 * dt + fq;
+          vf = *reinterpret_cast<const f16x8*>(st + KBYTES + vr * VV_PITCH + 16 * ((4 * hh + g) ^ vswz_key(vr)));
+        }
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[dt], 0, 0, 0);
       }
     }
@@ -1077,7 +1167,7 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
   }
 }
 
-template <int D, bool QK8>
+template <int D, bool QK8, bool VROW = false>
 hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, int64_t vt_ld, void* o, int64_t ldo,
                        int batch, int heads, int tokens, float sl2, bool out_fp8, float out_scale, hipStream_t s) {
   const int nqb = (tokens + QB - 1) / QB;
@@ -1094,19 +1184,19 @@ hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, 
       const f16* q16 = static_cast<const f16*>(q);
       const f16* k16 = static_cast<const f16*>(k);
       if (out_fp8)
-        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld, o, ldo,
-                           tokens, heads, nq16, sl2, out_scale);
+        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true, VROW>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld,
+                           o, ldo, tokens, heads, nq16, sl2, out_scale);
       else
-        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, false>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld, o,
-                           ldo, tokens, heads, nq16, sl2, out_scale);
+        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, false, VROW>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld,
+                           o, ldo, tokens, heads, nq16, sl2, out_scale);
       return hipGetLastError();
     }
   }
   if (out_fp8)
-    hipLaunchKernelGGL((flash_attn_vt_kernel<D, true, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((flash_attn_vt_kernel<D, true, VT_STAGES_DEFAULT, 3, 1, QK8, VROW>), dim3((unsigned)blocks),
                        dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
   else
-    hipLaunchKernelGGL((flash_attn_vt_kernel<D, false, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((flash_attn_vt_kernel<D, false, VT_STAGES_DEFAULT, 3, 1, QK8, VROW>), dim3((unsigned)blocks),
                        dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
   return hipGetLastError();
 }
@@ -1247,6 +1337,22 @@ hipError_t launch_flash_attention_vt(const void* q, const void* k, int64_t ld, i
     case 129: return launch_vt_d<64, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
     case 145: return launch_vt_d<72, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
     case 161: return launch_vt_d<80, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_flash_attention_vrow(const f16* q, const f16* k, const f16* v, int64_t ld, void* o, int64_t ldo,
+                                       int batch, int heads, int tokens, int head_dim, float scale, bool out_fp8,
+                                       float out_scale, hipStream_t s) {
+  if (batch < 1 || heads < 1 || tokens < 1 || !flash_attention_vt_supported(head_dim) ||
+      !qk_args_ok(q, k, ld, heads, head_dim, 0) || (reinterpret_cast<uintptr_t>(v) & 15) ||
+      ldo < (int64_t)heads * head_dim || (ldo & 3))
+    return hipErrorInvalidValue;
+  const float sl2 = scale * 1.4426950408889634f;
+  switch (head_dim) {
+    case 64: return launch_vt_d<64, false, true>(q, k, ld, v, 0, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 72: return launch_vt_d<72, false, true>(q, k, ld, v, 0, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
+    case 80: return launch_vt_d<80, false, true>(q, k, ld, v, 0, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, s);
   }
   return hipErrorInvalidValue;
 }

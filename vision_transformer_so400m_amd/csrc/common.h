@@ -175,6 +175,14 @@ hipError_t launch_flash_attention_vt(const void* q, const void* k, int64_t ld, i
                                      int64_t vt_ld, void* o, int64_t ldo, int batch, int heads, int tokens,
                                      int head_dim, float scale, bool out_fp8, float out_scale, hipStream_t s);
 
+// The same streaming attention with V row-major: q, k and v F16 with one row
+// stride ld (elements; a multiple of 8), head h at column h * head_dim of
+// each, v 16-byte aligned; head_dim 64, 72 or 80. The kernel reads V rows
+// and transposes them in its LDS reads, so no V^T buffer is needed.
+hipError_t launch_flash_attention_vrow(const f16* q, const f16* k, const f16* v, int64_t ld, void* o, int64_t ldo,
+                                       int batch, int heads, int tokens, int head_dim, float scale, bool out_fp8,
+                                       float out_scale, hipStream_t s);
+
 // The same with the PV product in e4m3: vt holds codes of v * v_scale (bytes,
 // row stride vt_ld, a multiple of 16, zero codes in columns tokens..vt_ld-1;
 // only each head's head_dim rows are read), the probabilities are quantized

@@ -125,7 +125,8 @@ struct siglip_model {
   float op_scale = 1.0f;   // operand quantization multiplier 2^-exp
   float acc_scale = 1.0f;  // product rescale 2^(2 exp)
   int patch_pad = 0, mlp_pad = 0;
-  bool vt_path = false;  // V written transposed by the QKV GEMM for the streaming attention
+  bool vt_path = false;  // streaming attention (head dims 64, 72, 80): V^T buffer in the workspace
+  bool vrow_ok = false;  // F16 attention products: one-round calls read V row-major instead (vrow_call)
   bool attn_fp8 = false; // PV product in e4m3: V^T as e4m3 codes of v * attn_v_scale
   bool attn_qk8 = false; // QK product in e4m3: Q and K as e4m3 codes of x * attn_v_scale in the
                          // QKV buffer's bytes, head h of a token row at byte h * 80 (K after Q)
@@ -412,7 +413,7 @@ GemmArgs qkv_args(siglip_model* m, const Gemm& g, const void* a, f16* c, void* v
 // its bytes), V transposed per head into vt when the streaming attention is
 // used.
 void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* vt, int M, hipStream_t s,
-              const LnFold* ln) {
+              const LnFold* ln, bool vrow) {
   const Gemm& g = Ly.qkv;
   const int W = m->width;
   uint8_t* qk8 = reinterpret_cast<uint8_t*>(qkv);
@@ -429,7 +430,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* v
       gemm(m, Ly.q, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
       gemm(m, Ly.k, a, W, M, qkv + W, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
     }
-    if (!m->vt_path) {
+    if (!m->vt_path || vrow) {
       gemm(m, Ly.v, a, W, M, qkv + 2 * W, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
       return;
     }
@@ -438,7 +439,7 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* v
               "v gemm launch");
     return;
   }
-  if (!m->vt_path) {
+  if (!m->vt_path || vrow) {
     gemm(m, g, a, W, M, qkv, 3 * W, EPI_BIAS, false, nullptr, 0, s, ln);
     return;
   }
@@ -453,6 +454,15 @@ void gemm_qkv(siglip_model* m, const Layer& Ly, const void* a, f16* qkv, void* v
 void capture(siglip_model* m, int stage, const void* src, size_t bytes, hipStream_t s) {
   if (m->capture_layer < 0 || !m->cap[stage]) return;
   hip_check(hipMemcpyAsync(m->cap[stage], src, bytes, hipMemcpyDeviceToDevice, s), "capture copy");
+}
+
+// Whether a call of `batch` images reads V row-major: with F16 attention
+// products, when the attention grid is one round (the 16-query kernel). V
+// then stays in the QKV rows and no V^T is written; larger grids run faster
+// on V^T (the 32-query kernel's transposing V reads cost more than the V^T
+// stores save). Both give the same bits.
+bool vrow_call(const siglip_model* m, int batch) {
+  return m->vrow_ok && (int64_t)((m->tokens + 127) / 128) * m->heads * batch <= 256;
 }
 
 void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int64_t* cols, int64_t* ld,
@@ -472,11 +482,11 @@ void stage_shape(const siglip_model* m, int stage, int batch, int64_t* rows, int
         b = 1;
       } else {
         l = 3LL * m->width;
-        c = m->vt_path ? 2LL * m->width : l;
+        c = m->vt_path && !vrow_call(m, batch) ? 2LL * m->width : l;
       }
       break;
     case SIGLIP_STAGE_V_T:
-      r = m->vt_path ? (int64_t)batch * m->heads * m->head_dim : 0;
+      r = m->vt_path && !vrow_call(m, batch) ? (int64_t)batch * m->heads * m->head_dim : 0;
       c = m->tokens;
       l = m->tokens_pad;
       b = m->attn_fp8 ? 1 : 2;
@@ -547,7 +557,8 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
     LaunchTimer lt(m, SIGLIP_K_EMBED, s);
     gemm(m, m->embed, A.xp, m->patch_pad, M, A.h, W, EPI_BIAS_POS, false, nullptr, 0, s);
   }
-  if (m->vt_path && m->tokens_pad > m->tokens) {
+  const bool vrow = vrow_call(m, B);  // V row-major in the QKV rows, no V^T
+  if (m->vt_path && !vrow && m->tokens_pad > m->tokens) {
     // V^T columns past the last token are read by the last key block: zeros
     LaunchTimer lt(m, SIGLIP_K_INPUT, s);
     const int64_t vrows = (int64_t)B * m->heads * m->head_dim;
@@ -578,12 +589,12 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
     {
       LaunchTimer lt(m, SIGLIP_K_QKV, s);
       if (m->ln_fold)
-        gemm_qkv(m, Ly, A.h, A.qkv, A.vt, M, s, &ln1);
+        gemm_qkv(m, Ly, A.h, A.qkv, A.vt, M, s, &ln1, vrow);
       else
-        gemm_qkv(m, Ly, A.a, A.qkv, A.vt, M, s, nullptr);
+        gemm_qkv(m, Ly, A.a, A.qkv, A.vt, M, s, nullptr, vrow);
     }
     if (ci) capture(m, SIGLIP_STAGE_QKV, A.qkv, cb(SIGLIP_STAGE_QKV), s);
-    if (ci && m->vt_path) capture(m, SIGLIP_STAGE_V_T, A.vt, cb(SIGLIP_STAGE_V_T), s);
+    if (ci && m->vt_path && !vrow) capture(m, SIGLIP_STAGE_V_T, A.vt, cb(SIGLIP_STAGE_V_T), s);
     {
       LaunchTimer lt(m, SIGLIP_K_ATTENTION, s);
       // Q and K: F16 columns of the QKV rows, or e4m3 head slots in their bytes
@@ -597,6 +608,10 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
         hip_check(launch_flash_attention_vt8(aq, ak, ald, apitch, static_cast<const uint8_t*>(A.vt), m->tokens_pad,
                                              A.o, W, B, m->heads, m->tokens, m->head_dim, attn_scale, q8,
                                              m->op_scale, m->attn_v_scale, s),
+                  "attention");
+      else if (vrow)
+        hip_check(launch_flash_attention_vrow(A.qkv, A.qkv + W, A.qkv + 2 * W, 3 * W, A.o, W, B, m->heads, m->tokens,
+                                              m->head_dim, attn_scale, q8, m->op_scale, s),
                   "attention");
       else if (m->vt_path)
         hip_check(launch_flash_attention_vt(aq, ak, ald, apitch, static_cast<const f16*>(A.vt), m->tokens_pad,
@@ -867,16 +882,21 @@ int create_impl(const void* blob, size_t blob_bytes, const siglip_options* opt, 
     m->acc_scale = std::ldexp(1.0f, 2 * m->scale_exp);
     m->patch_pad = (int)round_up(P, kKAlign);
     m->mlp_pad = (int)round_up(F, kNAlign);  // U is both an N (MLP up) and a K (MLP down) dimension
-    m->vt_path = flash_attention_vt_supported(m->head_dim);
     m->tokens_pad = (int)round_up(T, 64);
     m->separate_qkv = opt->separate_qkv == 1;
     m->ln_fold = opt->layernorm_fold == 1;
     m->attn_fp8 = (opt->attention_fp8 & 1) != 0;
     m->attn_qk8 = (opt->attention_fp8 & 2) != 0;
-    if ((m->attn_fp8 || m->attn_qk8) && !m->vt_path) {
+    // The streaming attention kernels take head widths 64, 72 and 80: with F16
+    // products they read V in the QKV rows; the e4m3 forms read V^T, which
+    // the QKV GEMM then writes.
+    const bool streaming = flash_attention_vt_supported(m->head_dim);
+    if ((m->attn_fp8 || m->attn_qk8) && !streaming) {
       delete m;
       return fail(SIGLIP_E_UNSUPPORTED, "attention_fp8 needs head_dim 64, 72 or 80");
     }
+    m->vt_path = streaming;
+    m->vrow_ok = streaming && !m->attn_fp8 && !m->attn_qk8;
     m->attn_v_scale = std::ldexp(1.0f, -opt->fp8_scale_exp);
     m->map_fold = opt->map_explicit_kv == 0 && map_fold_supported(W, m->heads, m->head_dim, T);
 
