@@ -25,7 +25,9 @@
 // cross-half shuffle), rescales, and computes O^T += V^T P^T where the P
 // fragment is the F32 score registers converted to F16 in place (the K
 // order inside a 16-key step is chosen to match the score layout, and V^T
-// is read in that same order).
+// is read in that same order). The row-major V form (VROW) reads V in its
+// token rows and transposes it in the LDS reads instead, with the same
+// products in the same order.
 //
 // map_attn: MAP-head probe attention, one query per (image, head) against the
 // T encoder tokens (page "Single-layer SigLIP vision benchmark", intro: one
