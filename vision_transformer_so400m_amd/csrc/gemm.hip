@@ -583,7 +583,8 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
 template <bool FP8, int EPI, bool OUT_FP8>
 hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // Tile choice measured on the batch-64 shapes (M = 46,656): the GELU
-  // epilogue takes 256x128 tiles, long-K or wide residual/QKV GEMMs 192x384,
+  // epilogue takes 128x256 tiles (256x128 where N % 256 != 0), long-K or
+  // wide residual/QKV GEMMs 192x384,
   // other N divisible by 256 256x256 tiles of eight waves (128x64 each, one
   // workgroup per CU), the rest 128x128 tiles of eight waves (64x32 each)
   // with two LDS stages, two workgroups per CU. Small M falls back to
