@@ -133,8 +133,9 @@ __device__ __forceinline__ void dma16(const void* gsrc, void* lds_wave_base) {
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-// MINW: workgroups per CU the register allocation must allow (2 for the tile
-// that relies on two workgroups sharing a CU).
+// MINW: waves per SIMD the register allocation must allow (the second
+// __launch_bounds__ argument): 2 for the four-wave tiles that rely on two
+// workgroups sharing a CU, 4 for eight-wave ones.
 // LNA: the A operand is LayerNorm-folded (GemmArgs::ln_stats): A rows are
 // the F16 residual, normalized in registers and written to LDS as operand
 // values; only the weight rows stream by DMA.
@@ -597,7 +598,10 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     if (g.ln_stats) {
       GemmArgs b = g;
       if (b.group_m == 0 && tiles_128 >= 1024) b.group_m = 8;
-      return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8, kRowBytes, 1, true>(b, s);
+      // two workgroups per CU where the registers allow it without spills (the
+      // GELU epilogue: 128 VGPRs; 864 -> 600 us at 46,656 x 4,352 x 1,152)
+      constexpr int LW = EPI == EPI_BIAS_GELU && (OUT_FP8 || !FP8) ? 4 : 1;
+      return launch_cfg<128, 128, 64, 32, 2, FP8, EPI, OUT_FP8, kRowBytes, LW, true>(b, s);
     }
   } else {
     if (g.ln_stats) return hipErrorInvalidValue;
