@@ -270,6 +270,28 @@ def test_attention_small_batch_kernel_matches_full_grid_kernel_bitwise(V, d):
     assert_close(f"one-round d{d}", one, ref, extra=_attn_extra(v[2:3], heads, d) + 1e-6)
 
 
+@pytest.mark.parametrize("t", [200, 256, 300])
+def test_attention_full_grid_last_block_forms(V, t):
+    """Grids above one round (nine images x 16 heads) run the 32-query kernel,
+    whose last key block is half (t = 200: keys 224.. are all padding and
+    left out), whole without padding (256) or whole with masked keys (300);
+    every form meets the oracle's bar and gives the bits the 16-query kernel
+    gives for the same image."""
+    b, heads, d = 9, 16, 72
+    w = heads * d
+    _flush(f"attention full grid, last block t={t}")
+    rng = np.random.default_rng(500 + t)
+    q, k, v = (rng.standard_normal((b, t, w), dtype=np.float32).astype(np.float16) for _ in range(3))
+    scale = 1 / math.sqrt(d)
+    full = V.attention(*(torch.from_numpy(a).cuda() for a in (q, k, v)), heads, d, scale)
+    one = V.attention(*(torch.from_numpy(a[8:9].copy()).cuda() for a in (q, k, v)), heads, d, scale)
+    torch.cuda.synchronize()
+    full, one = full.cpu().numpy(), one.cpu().numpy()
+    np.testing.assert_array_equal(one[0].view(np.uint16), full[8].view(np.uint16))
+    ref = _attn_ref(q, k, v, heads, d, scale)
+    assert_close(f"full grid t{t}", full, ref, extra=_attn_extra(v, heads, d) + 1e-6)
+
+
 def test_attention_binding_rejects_bad_tensors_before_launch(V):
     heads, d, t, b = 2, 72, 65, 2
     w = heads * d

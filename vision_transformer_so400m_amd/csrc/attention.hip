@@ -25,15 +25,22 @@
 // cross-half shuffle), rescales, and computes O^T += V^T P^T where the P
 // fragment is the F32 score registers converted to F16 in place (the K
 // order inside a 16-key step is chosen to match the score layout, and V^T
-// is read in that same order). The row-major V form (VROW) reads V in its
-// token rows and transposes it in the LDS reads instead, with the same
-// products in the same order.
+// is read in that same order). The small-batch kernel's row-major V form
+// (VROW) reads V in its token rows and transposes it in the LDS reads
+// instead, with the same products in the same order.
+//
+// Padding work that is skipped: a wave whose queries all lie past T only
+// helps move K and V into LDS, and a last key block whose second 32-key half
+// lies past T leaves that half out (its probabilities would be exact zeros).
 //
 // map_attn: MAP-head probe attention, one query per (image, head) against the
 // T encoder tokens (page "Single-layer SigLIP vision benchmark", intro: one
 // shared learned probe, its own query projection, one fused KV projection).
 // Memory-bound: it reads K and V once (2 x T x 72 x 2 bytes per head).
 #include "common.h"
+
+#include <type_traits>
+
 
 namespace siglip {
 namespace {
@@ -356,23 +363,20 @@ __device__ __forceinline__ f16x8 cat8(f16x4 lo, f16x4 hi) {
 
 // QK8: q and k are e4m3 codes (head h of a token row at byte h * kQK8Pitch,
 // ld in bytes), their products scaled into c by the caller.
-// VROW: vt is V row-major (rows of stride ld, head h at column h * D, as q
-// and k), read through the transposing LDS reads; vt_ld is not used.
-template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1, bool QK8 = false,
-          bool VROW = false>
+template <int D, bool OUT_FP8, int VT_STAGES = VT_STAGES_DEFAULT, int MIN_WG = 3, int QT = 1, bool QK8 = false>
 __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D <= 80 && D >= 64, "head width");
   static_assert(QT == 1 || QT == 2, "query tiles per wave");
   static_assert(!QK8 || QT == 1, "e4m3 Q/K with one query tile per wave");
-  static_assert(!VROW || (!QK8 && QT == 1), "row-major V with F16 Q/K, one query tile per wave");
   constexpr int QWG = 4 * 32 * QT;               // queries per workgroup
   constexpr int NDC = D / 8;                     // 16-byte dim chunks per key
   constexpr int KBYTES = QK8 ? VK8_BYTES : VK_BYTES;
-  constexpr int STAGE = KBYTES + (VROW ? VR_BYTES : VROWS * VV_PITCH);
+  constexpr int STAGE = KBYTES + VROWS * VV_PITCH;
   constexpr int NK = KBYTES / 1024;              // 1 KiB transfers for K per stage
-  constexpr int NDMA = NK + (VROW ? VR_BYTES / 1024 : D / 8);  // 1 KiB transfers per stage
+  static_assert(KBYTES % 1024 == 0, "whole K transfers");
+  constexpr int NDMA = NK + D / 8;               // 1 KiB transfers per stage
   constexpr int PER_WAVE = (NDMA + 3) / 4;       // every wave issues the same count
   constexpr int RL = (D - 64) / 2;               // oacc[.][2] register holding O^T row D (lane group 0)
   constexpr float kTau = 8.0f;                   // rescale only when a row max grows by > 2^8
@@ -428,8 +432,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   // constant V^T rows of every stage: row D = 1 (the PV product then also
   // yields each query's sum of the F16 probabilities it used), rows D+1..95 = 0
   // (row-major V brings its padding with every transfer)
-  if constexpr (VROW) vrow_pad<NDC>(smem, VT_STAGES, STAGE, KBYTES, t, 256);
-  constexpr int ZCH = VROW ? 0 : (VROWS - D) * VV_PITCH / 16;
+  constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
   for (int i = t; i < VT_STAGES * ZCH; i += 256) {
     const int r = i % ZCH;
     uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
@@ -449,13 +452,6 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   for (int j = 0; j < PER_WAVE; ++j) {
     const int jg = wave + 4 * j;
     const int off = jg * 1024 + 16 * lane;
-    if (VROW && jg >= NK && jg < NDMA) {  // V row kkey, chunk kdc (>= NDC: padding, not transferred)
-      const int vo = off - NK * 1024;
-      kkey[j] = vo / kVRowPitch;
-      kdc[j] = (vo % kVRowPitch) / 16;
-      src[j] = vt + (img + kkey[j]) * ld + hc + 8 * min(kdc[j], NDC - 1);
-      continue;
-    }
     if constexpr (QK8) {  // K row of kQK8Pitch code bytes: 5 chunks of 16
       kkey[j] = key_of_row(off / kQK8Pitch);
       kdc[j] = (off % kQK8Pitch) / 16;
@@ -475,32 +471,40 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
       src[j] = vth;
     }
   }
+  // bytes a slot's source advances per key (uniform): K rows by ld, V^T
+  // columns by one F16, padding slots not at all
+  int64_t kstep[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int jg = wave + 4 * j;
+    kstep[j] = jg < NK ? (QK8 ? ld : 2 * ld) : jg < NDMA ? 2 : 0;
+  }
   auto issue = [&](int kb) {
     const int key0 = kb * KB;
     uint8_t* st = smem + (kb % VT_STAGES) * STAGE;
     const bool tail = key0 + KB > T;  // keys past T re-read token T-1
+    if (!tail) {
+      // every slot lands at its KiB of the stage (the V^T part starts at
+      // NK KiB), padding slots in the trash KiB: no per-slot branches
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int jg = wave + 4 * j;
+        dma16(reinterpret_cast<const uint8_t*>(src[j]) + key0 * kstep[j], jg < NDMA ? st + jg * 1024 : trash);
+      }
+      return;
+    }
+    // the last block: K rows past T re-read token T-1 (V^T columns past T
+    // are zeros in memory)
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int jg = wave + 4 * j;
       if (jg < NK) {
-        const void* p;
         if constexpr (QK8)
-          p = tail ? kb8 + (img + min(key0 + kkey[j], T - 1)) * ld + h * kQK8Pitch + 16 * kdc[j]
-                   : reinterpret_cast<const uint8_t*>(src[j]) + (int64_t)key0 * ld;
+          dma16(kb8 + (img + min(key0 + kkey[j], T - 1)) * ld + h * kQK8Pitch + 16 * kdc[j], st + jg * 1024);
         else
-          p = tail ? k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
-                   : src[j] + (int64_t)key0 * ld;
-        dma16(p, st + jg * 1024);
-      } else if (jg < NDMA) {
-        if constexpr (VROW) {
-          const f16* p = tail ? vt + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j]
-                              : src[j] + (int64_t)key0 * ld;
-          if (kdc[j] < NDC) dma16(p, st + jg * 1024);
-        } else {
-          dma16(src[j] + key0, st + KBYTES + (jg - NK) * 1024);
-        }
+          dma16(k + (img + min(key0 + kkey[j], T - 1)) * ld + hc + 8 * kdc[j], st + jg * 1024);
       } else {
-        dma16(src[j], trash);
+        dma16(reinterpret_cast<const uint8_t*>(src[j]) + key0 * kstep[j], jg < NDMA ? st + jg * 1024 : trash);
       }
     }
   };
@@ -510,12 +514,6 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   int voff[4];                                                   // + dt*32*128
 #pragma unroll
   for (int s = 0; s < 4; ++s) voff[s] = KBYTES + fr * VV_PITCH + 16 * ((2 * s + fg) ^ vswz_key(fr));
-  // VROW: lane a + 4r of 16-lane group G reads dims 16 (G & 1) + 4a .. + 3 of
-  // key 8 (G >> 1) + r (+ 16 s + 4 t for PV k-step s, half t; + 32 dt dims):
-  // lane 4a + b then holds dim 16 (G & 1) + 4a + b = fr of keys
-  // 16 s + 8 fg + 4 t + 0..3, the A operand of the 32x32x16 product
-  const int vrb = KBYTES + (8 * (lane >> 5) + ((lane & 15) >> 2)) * kVRowPitch +
-                  2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   float m_run[QT];
   f32x16 oacc[QT][3];
@@ -528,24 +526,17 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
       for (int r = 0; r < 16; ++r) oacc[u][dt][r] = 0.0f;
   }
 
-  const int nkb = (T + KB - 1) / KB;
-#pragma unroll
-  for (int p = 0; p < VT_STAGES - 1; ++p)
-    if (p < nkb) issue(p);
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + VT_STAGES - 2 < nkb)
-      attn_wait_vmcnt<(VT_STAGES - 2) * PER_WAVE>();
-    else
-      attn_wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    if (kb + VT_STAGES - 1 < nkb) issue(kb + VT_STAGES - 1);  // into the stage block kb-1 used
-    const uint8_t* st = smem + (kb % VT_STAGES) * STAGE;
-    const int key0 = kb * KB;
-
+  // One 64-key block. NKT: 32-key score tiles that hold a key below T (2,
+  // or 1 for a last block whose second half is all padding: its scores
+  // would be -inf, its probabilities 0 and its products exact zeros, so
+  // leaving that half out gives the same bits).
+  auto block = [&](const uint8_t* st, int key0, auto nkt_tag, auto tail_tag) {
+    constexpr int NKT = decltype(nkt_tag)::value;
+    constexpr bool TAIL = decltype(tail_tag)::value;  // the last block: keys past T masked
     // S^T for every query tile; each K fragment read feeds QT MFMAs
-    f32x16 sacc[QT][2];
+    f32x16 sacc[QT][NKT];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
       for (int u = 0; u < QT; ++u)
 #pragma unroll
@@ -567,11 +558,11 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
         }
       }
     }
-    if (key0 + KB > T) {
+    if (TAIL && key0 + KB > T) {
 #pragma unroll
       for (int u = 0; u < QT; ++u)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (key0 + key_of_row(32 * kt + 8 * (r >> 2) + 4 * fg + (r & 3)) >= T) sacc[u][kt][r] = kNegInf;
@@ -581,8 +572,10 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     for (int u = 0; u < QT; ++u) {
       float a[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        a[i] = fmaxf(fmaxf(sacc[u][0][i], sacc[u][0][i + 8]), fmaxf(sacc[u][1][i], sacc[u][1][i + 8]));
+      for (int i = 0; i < 8; ++i) {
+        a[i] = fmaxf(sacc[u][0][i], sacc[u][0][i + 8]);
+        if constexpr (NKT == 2) a[i] = fmaxf(a[i], fmaxf(sacc[u][NKT - 1][i], sacc[u][NKT - 1][i + 8]));
+      }
       float mx = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
       mx = half_swap_max(mx);
       // Probabilities are exp(scale (s - m_run)) with a running reference
@@ -602,7 +595,7 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
     }
 
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2 * NKT; ++s) {
       const int kt = s >> 1, base = 8 * (s & 1);
       f16x8 pf[QT];
 #pragma unroll
@@ -618,17 +611,45 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
         }
 #pragma unroll
       for (int dt = 0; dt < 3; ++dt) {  // keys 16s + 8fg + (0..7) of dim row 32dt + fr
-        f16x8 vf;
-        if constexpr (VROW) {
-          const uint8_t* pv = st + vrb + 16 * s * kVRowPitch + 64 * dt;
-          vf = cat8(ds_read_tr4(pv), ds_read_tr4(pv + 4 * kVRowPitch));
-        } else {
-          vf = *reinterpret_cast<const f16x8*>(st + voff[s] + dt * 32 * VV_PITCH);
-        }
+        const f16x8 vf = *reinterpret_cast<const f16x8*>(st + voff[s] + dt * 32 * VV_PITCH);
 #pragma unroll
         for (int u = 0; u < QT; ++u)
           oacc[u][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[u], oacc[u][dt], 0, 0, 0);
       }
+    }
+  };
+
+  // A wave whose queries all lie past T only moves K/V^T for the others.
+  // The last block (keys past T masked, possibly only its first half) runs
+  // after the loop, so the loop holds one form of the block.
+  const bool active = qb * QWG + wave * QT * 32 < T;
+  const int nkb = (T + KB - 1) / KB;
+  using full = std::integral_constant<int, 2>;
+  using half = std::integral_constant<int, 1>;
+  using yes = std::true_type;
+  using no = std::false_type;
+#pragma unroll
+  for (int p = 0; p < VT_STAGES - 1; ++p)
+    if (p < nkb) issue(p);
+  for (int kb = 0; kb < nkb - 1; ++kb) {
+    if (kb + VT_STAGES - 2 < nkb)
+      attn_wait_vmcnt<(VT_STAGES - 2) * PER_WAVE>();
+    else
+      attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + VT_STAGES - 1 < nkb) issue(kb + VT_STAGES - 1);  // into the stage block kb-1 used
+    if (active) block(smem + (kb % VT_STAGES) * STAGE, kb * KB, full(), no());
+  }
+  {
+    const int kb = nkb - 1, key0 = kb * KB;
+    attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const uint8_t* st = smem + (kb % VT_STAGES) * STAGE;
+    if (active) {
+      if (key0 + 32 >= T)
+        block(st, key0, half(), yes());
+      else
+        block(st, key0, full(), yes());
     }
   }
 
@@ -939,13 +960,14 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
 
 // ---------------------------------------------------------------------------
 // The same attention for one-round grids (small batches): 16 queries per
-// wave with v_mfma_f32_16x16x32_f16, eight waves (128 queries) per
-// workgroup, two workgroups per CU. Per query it does the same products,
-// exponentials and rescales in the same order as flash_attn_vt_kernel, so
-// its outputs are bit-identical (tested); each wave's chain of dependent
-// steps per key block is half as long, which is what a grid of one round
-// waits on, while a full grid runs faster on the 32-query kernel, whose
-// waves read each K/V^T fragment once for twice the queries.
+// wave with v_mfma_f32_16x16x32_f16, four waves (64 queries) per
+// workgroup, so a batch-1 grid of 729 tokens x 16 heads is 192 workgroups of
+// one wave per SIMD. Per query it does the same products, exponentials and
+// rescales in the same order as flash_attn_vt_kernel, so its outputs are
+// bit-identical (tested); each wave's chain of dependent steps per key block
+// is half as long, which is what a grid of one round waits on, while a full
+// grid runs faster on the 32-query kernel, whose waves read each K/V^T
+// fragment once for twice the queries.
 //
 // K rows are stored permuted within each 32-key half: LDS row
 // 32h + 16t + 4g + i holds key 32h + 8g + 4t + i, so lane group g of score
@@ -954,13 +976,15 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
 // h. A K row has D/8 (made odd) 16-byte chunks: conflict-free fragment reads
 // of 16 consecutive rows; dims past D read the last real chunk, against zero
 // Q padding. V^T rows D (ones: the probability sum) .. 16 NT - 1 (zeros) are
-// written once. VROW: vt is V row-major, as for flash_attn_vt_kernel.
+// written once. VROW: vt is V row-major (rows of stride ld, head h at column
+// h * D, as q and k), read through the transposing LDS reads; vt_ld is not
+// used.
 template <int D, bool OUT_FP8, bool VROW = false>
-__global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
+__global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
     const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D >= 64 && D <= 80, "head width");
-  constexpr int NW = 8;
+  constexpr int NW = 4;
   constexpr int QWG = NW * 16;
   constexpr int NDC = D / 8;                       // 16-byte dim chunks of a key
   constexpr int KP = 16 * (NDC | 1);               // K LDS row pitch (odd chunk count)
@@ -975,8 +999,9 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
   constexpr int NDMA = NK + (VROW ? VR_BYTES / 1024 : D / 8);  // and for V (V^T: 8 rows of 128 bytes each)
   constexpr int PER_WAVE = (NDMA + NW - 1) / NW;
   constexpr float kTau = 8.0f;                     // rescale only when a row max grows by > 2^8
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + 1024];
-  uint8_t* trash = smem + 2 * STAGE;
+  constexpr int STAGES = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 1024];
+  uint8_t* trash = smem + STAGES * STAGE;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -1004,9 +1029,9 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
       qf[ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   __builtin_amdgcn_s_waitcnt(0);  // as in flash_attn_vt_kernel: Q complete before the block loop
-  if constexpr (VROW) vrow_pad<NDC>(smem, 2, STAGE, KBYTES, t, NW * 64);
+  if constexpr (VROW) vrow_pad<NDC>(smem, STAGES, STAGE, KBYTES, t, NW * 64);
   constexpr int ZCH = VROW ? 0 : (VR - D) * VV_PITCH / 16;
-  for (int i = t; i < 2 * ZCH; i += NW * 64) {
+  for (int i = t; i < STAGES * ZCH; i += NW * 64) {
     const int r = i % ZCH;
     uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
     const int one = 0x3C003C00;  // two F16 ones
@@ -1040,10 +1065,31 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
       src[j] = vth;
     }
   }
+  // per slot: bytes its source advances per key (uniform) and whether this
+  // lane transfers (row-major V lanes that would land on padding do not)
+  int64_t kstep[PER_WAVE];
+  bool lon[PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int jg = wave + NW * j;
+    kstep[j] = jg < NK ? 2 * ld : jg < NDMA ? (VROW ? 2 * ld : 2) : 0;
+    lon[j] = !(VROW && jg >= NK && jg < NDMA && kdc[j] >= NDC);
+  }
   auto issue = [&](int kb) {
     const int key0 = kb * KB;
-    uint8_t* st = smem + (kb & 1) * STAGE;
+    uint8_t* st = smem + (kb % STAGES) * STAGE;
     const bool tail = key0 + KB > T;  // keys past T re-read token T-1
+    if (!tail) {
+      // every slot lands at its KiB of the stage (the V part starts at NK
+      // KiB), padding slots in the trash KiB: no per-slot branches
+#pragma unroll
+      for (int j = 0; j < PER_WAVE; ++j) {
+        const int jg = wave + NW * j;
+        if (lon[j])
+          dma16(reinterpret_cast<const uint8_t*>(src[j]) + key0 * kstep[j], jg < NDMA ? st + jg * 1024 : trash);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int jg = wave + NW * j;
@@ -1078,17 +1124,15 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
 #pragma unroll
   for (int dt = 0; dt < NT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nkb = (T + KB - 1) / KB;
-  issue(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    attn_wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();             // block kb in LDS; block kb-1's stage free
-    if (kb + 1 < nkb) issue(kb + 1);
-    const uint8_t* st = smem + (kb & 1) * STAGE;
-    const int key0 = kb * KB;
-    f32x4 sacc[4];  // S^T tile tt: LDS rows 16 tt + 4 g + i, query fq
+  // One 64-key block; NKT: 32-key halves that hold a key below T (a last
+  // block's all-padding second half would add exact zeros: left out, the
+  // same bits)
+  auto block = [&](const uint8_t* st, int key0, auto nkt_tag, auto tail_tag) {
+    constexpr int NKT = decltype(nkt_tag)::value;
+    constexpr bool TAIL = decltype(tail_tag)::value;  // the last block: keys past T masked
+    f32x4 sacc[2 * NKT];  // S^T tile tt: LDS rows 16 tt + 4 g + i, query fq
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 2 * NKT; ++tt) {
       sacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -1096,17 +1140,19 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
         sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ks], sacc[tt], 0, 0, 0);
       }
     }
-    if (key0 + KB > T) {
+    if (TAIL && key0 + KB > T) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 2 * NKT; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (key0 + 32 * (tt >> 1) + 8 * g + 4 * (tt & 1) + i >= T) sacc[tt][i] = kNegInf;
     }
     float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                      fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[2][0], sacc[2][1]), fmaxf(sacc[2][2], sacc[2][3])),
-                         fmaxf(fmaxf(sacc[3][0], sacc[3][1]), fmaxf(sacc[3][2], sacc[3][3]))));
+    if constexpr (NKT == 2)
+      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sacc[NKT][0], sacc[NKT][1]), fmaxf(sacc[NKT][2], sacc[NKT][3])),
+                           fmaxf(fmaxf(sacc[2 * NKT - 1][0], sacc[2 * NKT - 1][1]),
+                                 fmaxf(sacc[2 * NKT - 1][2], sacc[2 * NKT - 1][3]))));
     {  // over the four lane groups of query fq: lane rows 0/1 and 2/3, then the halves
       unsigned a = __builtin_bit_cast(unsigned, mx), bb = a;
       asm volatile("" : "+v"(bb));  // two distinct operands (see half_swap)
@@ -1124,7 +1170,7 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
     }
     const float mc = m_run * c;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {  // PV k-step: keys 32 hh + 8 g .. + 7 of this lane group
+    for (int hh = 0; hh < NKT; ++hh) {  // PV k-step: keys 32 hh + 8 g .. + 7 of this lane group
       f16x8 pf;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -1148,6 +1194,42 @@ __global__ __launch_bounds__(512, 2) void flash_attn_vt16_kernel(
         }
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[dt], 0, 0, 0);
       }
+    }
+  };
+
+  // a wave whose queries all lie past T only moves K/V for the others; the
+  // last block (keys past T masked, possibly only its first half) runs
+  // after the loop, so the loop holds one form of the block
+  const bool active = qb * QWG + wave * 16 < T;
+  const int nkb = (T + KB - 1) / KB;
+  using full = std::integral_constant<int, 2>;
+  using half = std::integral_constant<int, 1>;
+  using yes = std::true_type;
+  using no = std::false_type;
+  // every issue() is PER_WAVE transfer instructions of this wave (each slot
+  // has real lanes), so at most (STAGES - 2) blocks' worth may stay in flight
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < nkb) issue(p);
+  for (int kb = 0; kb < nkb - 1; ++kb) {
+    if (kb + STAGES - 2 < nkb)
+      attn_wait_vmcnt<(STAGES - 2) * PER_WAVE>();
+    else
+      attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // block kb in LDS; block kb-1's stage free
+    if (kb + STAGES - 1 < nkb) issue(kb + STAGES - 1);
+    if (active) block(smem + (kb % STAGES) * STAGE, kb * KB, full(), no());
+  }
+  {
+    const int kb = nkb - 1, key0 = kb * KB;
+    attn_wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const uint8_t* st = smem + (kb % STAGES) * STAGE;
+    if (active) {
+      if (key0 + 32 >= T)
+        block(st, key0, half(), yes());
+      else
+        block(st, key0, full(), yes());
     }
   }
   // the probability sum sits in O^T row D: tile D / 16, lane group (D % 16) / 4, register D % 4
@@ -1177,30 +1259,35 @@ hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, 
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   // One round of workgroups (batch 1 and 2 at 729 tokens x 16 heads): the
   // 16-query kernel, the same bits (729 tokens, 16 heads, head dim 72, batch
-  // 1 / 2: 20.2 -> 19.3 us, 21.5 -> 20.4 us; from batch 3 on the 32-query
-  // kernel is as fast or faster)
+  // 1 / 2: 20.2 -> 19.3 us, 21.5 -> 20.4 us with eight waves per workgroup;
+  // four waves, one per SIMD, 18.9 -> 16.4 us at batch 1; deeper K/V rings
+  // did not help; from batch 3 on the 32-query kernel is as fast or faster)
   if constexpr (!QK8) {
     if (blocks <= 256) {
-      const unsigned nb = (unsigned)((tokens + 127) / 128 * heads * batch);
-      const int nq16 = (tokens + 127) / 128;
+      const int nq16 = (tokens + 63) / 64;
+      const unsigned nb = (unsigned)(nq16 * heads * batch);
       const f16* q16 = static_cast<const f16*>(q);
       const f16* k16 = static_cast<const f16*>(k);
       if (out_fp8)
-        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true, VROW>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld,
+        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true, VROW>), dim3(nb), dim3(256), 0, s, q16, k16, ld, vt, vt_ld,
                            o, ldo, tokens, heads, nq16, sl2, out_scale);
       else
-        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, false, VROW>), dim3(nb), dim3(512), 0, s, q16, k16, ld, vt, vt_ld,
+        hipLaunchKernelGGL((flash_attn_vt16_kernel<D, false, VROW>), dim3(nb), dim3(256), 0, s, q16, k16, ld, vt, vt_ld,
                            o, ldo, tokens, heads, nq16, sl2, out_scale);
       return hipGetLastError();
     }
   }
-  if (out_fp8)
-    hipLaunchKernelGGL((flash_attn_vt_kernel<D, true, VT_STAGES_DEFAULT, 3, 1, QK8, VROW>), dim3((unsigned)blocks),
-                       dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
-  else
-    hipLaunchKernelGGL((flash_attn_vt_kernel<D, false, VT_STAGES_DEFAULT, 3, 1, QK8, VROW>), dim3((unsigned)blocks),
-                       dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
-  return hipGetLastError();
+  if constexpr (VROW) {
+    return hipErrorInvalidValue;  // row-major V: one-round grids only (the 16-query kernel)
+  } else {
+    if (out_fp8)
+      hipLaunchKernelGGL((flash_attn_vt_kernel<D, true, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
+                         dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
+    else
+      hipLaunchKernelGGL((flash_attn_vt_kernel<D, false, VT_STAGES_DEFAULT, 3, 1, QK8>), dim3((unsigned)blocks),
+                         dim3(256), 0, s, q, k, ld, vt, vt_ld, o, ldo, tokens, heads, nqb, sl2, out_scale);
+    return hipGetLastError();
+  }
 }
 
 constexpr int kMapMaxT = 4096;
