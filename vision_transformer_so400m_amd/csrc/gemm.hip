@@ -43,6 +43,7 @@
 
 #include <type_traits>
 
+
 namespace siglip {
 namespace {
 
@@ -365,6 +366,37 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
     }
   }
 
+  // Residual tiles whose F32 staged form takes more than one pass (the
+  // 192x384 tile) but whose F16 form fits the two-stage ring (RES_LDS): the
+  // F16 residual tile comes into the ring by DMA as 16-byte chunks, swizzled
+  // by row like the staged tiles of the epilogue. Half h of its rows fills
+  // stage h: the half whose stage is free while the last K slice is
+  // multiplied goes then, the other after the main loop. The residual rows
+  // are read and written by this workgroup only, so the early read is safe
+  // in place.
+  constexpr bool RES_LDS = EPI == EPI_BIAS_RES && STAGES == 2 && !LNA &&
+                           BM * BN * 8 > STAGES * T::STAGE && BM * BN * 2 == STAGES * T::STAGE;
+  constexpr int RROW = BN * 2;  // F16 bytes per residual tile row
+  constexpr int RCH = RROW / 16;
+  constexpr int RSWZ = (RCH % 16 == 0 ? 16 : RCH % 8 == 0 ? 8 : RCH % 4 == 0 ? 4 : RCH % 2 == 0 ? 2 : 1) - 1;
+  static_assert(RCH % (RSWZ + 1) == 0, "swizzled chunks stay inside the row");
+  auto raddr = [&](int r, int byte) -> uint8_t* {
+    return smem + r * RROW + ((((byte >> 4) ^ (r & RSWZ)) << 4) | (byte & 15));
+  };
+  constexpr int RDMA = BM / 2 * RCH / (64 * T::WAVES);  // 1 KiB transfers per wave and half
+  static_assert(!RES_LDS || (BM / 2 * RCH) % (64 * T::WAVES) == 0, "whole residual transfers");
+  auto res_dma = [&](int h) {
+#pragma unroll
+    for (int j = 0; j < RDMA; ++j) {
+      const int kib = (h * RDMA + j) * T::WAVES + wave;
+      const int slot = kib * 64 + lane;                    // LDS chunk this lane fills
+      const int r = slot / RCH;
+      const int c = (slot - r * RCH) ^ (r & RSWZ);          // the logical chunk kept there
+      const int m = min(m0 + r, g.M - 1);                    // rows past M: read, never stored
+      dma16(g.res + (int64_t)m * g.ldres + n0 + c * 8, smem + kib * 1024);
+    }
+  };
+
   if constexpr (LNA) {
     // Two stages. Iteration kt writes the A part of stage kt % 2, last read
     // by slice kt - 2's products, which every wave finished before the
@@ -398,6 +430,7 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
         wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      else if (RES_LDS && kt == nk - 1) res_dma(nk % 2);  // the stage slice kt-1 held
       compute(kt % STAGES);
     }
   }
@@ -439,6 +472,46 @@ __global__ __launch_bounds__(64 * (BM / WM) * (BN / WN), MINW) void gemm_kernel(
       }
       return;
     }
+  }
+  // Residual tiles whose F32 staged form takes more than one pass: the
+  // residual tile is in LDS (res_dma); each lane adds its accumulators to the
+  // residual values of its rows in registers and writes the F16 sums back in
+  // place (the same arithmetic as the staged path: acc * acc_scale is exact,
+  // then + bias, + residual, one F16 rounding), and the workgroup stores
+  // whole 16-byte row chunks.
+  if constexpr (RES_LDS) {
+    __syncthreads();  // every wave is done with the ring
+    res_dma(1 - nk % 2);  // the half the last slice's stage held
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * WN + j * 32 + 8 * q + 4 * fg;
+        const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + n0 + c);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+          f16x4* p = reinterpret_cast<f16x4*>(raddr(wm * WM + i * 32 + fr, 2 * c));
+          const f16x4 rv = *p;
+          f16x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = (f16)((acc[i][j][4 * q + e] * g.acc_scale + b[e]) + (float)rv[e]);
+          *p = o;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int u = t; u < BM * RCH; u += T::THREADS) {
+      const int rs = u / RCH;
+      const int c = (u - rs * RCH) * 8;
+      const int m = m0 + rs;
+      if (m >= g.M) continue;
+      *reinterpret_cast<i32x4*>(reinterpret_cast<f16*>(g.c) + (int64_t)m * g.ldc + n0 + c) =
+          *reinterpret_cast<const i32x4*>(raddr(rs, 2 * c));
+    }
+    return;
   }
   // Output through LDS. The MFMA layout gives each lane 4-column pieces of
   // 32 different rows, so direct stores write 4 or 8 bytes per row per
@@ -637,8 +710,11 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     // same bits. Twelve waves of 96x64 (164-167 VGPRs, three waves per SIMD
     // instead of two, to cover the slice waits and the epilogue) take a
     // 3456-wide projection from 221-231 to 207-215 us and MLP down from
-    // ~248 to 233-251 us, the same bits. The residual tile is staged in two
-    // bands. Not for the out-projection (K = 1152: 729 tiles leave a long
+    // ~248 to 233-251 us, the same bits. The residual tile comes into the
+    // ring by DMA, half of it during the last K slice, and is added in
+    // registers (RES_LDS; MLP down 234 -> 225 us against the F32 tile
+    // staged in two bands, 233 -> 229 us for the half issued early, the
+    // same bits). Not for the out-projection (K = 1152: 729 tiles leave a long
     // tail; 98 -> 105-113 us). A V-transposing tile must not straddle the V
     // columns.
     if constexpr (EPI == EPI_BIAS_RES || EPI == EPI_BIAS || EPI == EPI_QKV || EPI == EPI_QKV8) {
