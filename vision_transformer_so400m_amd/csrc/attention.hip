@@ -861,12 +861,15 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.0f;
 
+  // a wave whose queries all lie past T only moves K/V^T for the others
+  const bool active = qb * QWG + wave * 32 < T;
   const int nkb = (T + KB - 1) / KB;
   issue(0);
   for (int kb = 0; kb < nkb; ++kb) {
     attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     if (kb + 1 < nkb) issue(kb + 1);  // into the stage block kb-1 used
+    if (!active) continue;
     const uint8_t* st = smem + (kb % STAGES) * STAGE;
     const int key0 = kb * KB;
 

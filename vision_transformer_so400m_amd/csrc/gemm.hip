@@ -44,6 +44,7 @@
 #include <type_traits>
 
 
+
 namespace siglip {
 namespace {
 
@@ -657,8 +658,8 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
 template <bool FP8, int EPI, bool OUT_FP8>
 hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
   // Tile choice measured on the batch-64 shapes (M = 46,656): the GELU
-  // epilogue takes 128x256 tiles (256x128 where N % 256 != 0), long-K or
-  // wide residual/QKV GEMMs 192x384,
+  // epilogue takes 128x256 tiles (256x128 where N % 256 != 0), residual,
+  // long-K and wide QKV GEMMs 192x384 where N divides by 384,
   // other N divisible by 256 256x256 tiles of eight waves (128x64 each, one
   // workgroup per CU), the rest 128x128 tiles of eight waves (64x32 each)
   // with two LDS stages, two workgroups per CU. Small M falls back to
@@ -701,8 +702,8 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
       if (g.N % 256 == 0) return launch_cfg<128, 256, 64, 128, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
       return launch_cfg<256, 128, 128, 64, 3, FP8, EPI, OUT_FP8, 64, 2>(b, s);
     }
-    // Long K (MLP down, K = 4352) or wide N (the fused QKV projection, 3456;
-    // the explicit MAP K/V, 2304): 192x384 tiles, 2 stages, 144 KiB of LDS.
+    // Long K (MLP down, K = 4352), wide N (the fused QKV projection, 3456;
+    // the explicit MAP K/V, 2304) or a residual: 192x384 tiles, 2 stages, 144 KiB of LDS.
     // Per flop they move half the operand bytes of 128x128 tiles from L2
     // into LDS (A is re-read for 3 column blocks of 1152 instead of 9), which
     // is what bounds these GEMMs: at 46,656 rows MLP down 280 -> 245 us and a
@@ -714,13 +715,14 @@ hipError_t launch_sized(const GemmArgs& g, hipStream_t s) {
     // ring by DMA, half of it during the last K slice, and is added in
     // registers (RES_LDS; MLP down 234 -> 225 us against the F32 tile
     // staged in two bands, 233 -> 229 us for the half issued early, the
-    // same bits). Not for the out-projection (K = 1152: 729 tiles leave a long
-    // tail; 98 -> 105-113 us). A V-transposing tile must not straddle the V
-    // columns.
+    // same bits). The out-projection (K = 1152) takes them too since its
+    // residual is added that way: 95.8 -> 91.3 us per launch (with the F32
+    // tile in two bands it was 98 -> 105-113 us). A V-transposing tile must
+    // not straddle the V columns.
     if constexpr (EPI == EPI_BIAS_RES || EPI == EPI_BIAS || EPI == EPI_QKV || EPI == EPI_QKV8) {
       constexpr bool qkv = EPI == EPI_QKV || EPI == EPI_QKV8;
       const bool fits = g.N % 384 == 0 && (!qkv || g.vt_col0 % 384 == 0);
-      if (fits && ((int64_t)g.K * (FP8 ? 1 : 2) >= 2048 || g.N >= 2304)) {
+      if (fits && ((int64_t)g.K * (FP8 ? 1 : 2) >= 2048 || g.N >= 2304 || EPI == EPI_BIAS_RES)) {
         if (b.group_m == 0) b.group_m = 8;
         return launch_cfg<192, 384, 96, 64, 2, FP8, EPI, OUT_FP8>(b, s);
       }
