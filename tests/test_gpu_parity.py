@@ -561,21 +561,23 @@ def _band_rows(M):
     return sorted({r for blk in blocks for r in blk if 0 <= r < M})
 
 
-@pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
-def test_b64_layer0_stages_on_sampled_row_blocks(V, fp8):
-    """The batch-64 launch shapes (192x384 tiles for QKV and MLP-down,
-    128x256 for MLP-up, 128x128 for the out-projection, banded tile order,
-    the V-transposing and residual epilogues) element by element on sampled
-    row blocks, at one layer (stage capture runs the batch on one stream, so
-    every launch covers all 46,656 rows)."""
+@pytest.mark.parametrize("batch,fp8", [(64, False), (64, True), (24, True)], ids=["b64-f16", "b64-fp8", "b24-fp8"])
+def test_large_grid_layer0_stages_on_sampled_row_blocks(V, batch, fp8):
+    """The large-grid launch shapes (192x384 tiles for QKV, the
+    out-projection and MLP-down, 128x256 for MLP-up, banded tile order, the
+    V-transposing epilogue and the residual tile added from LDS) element by
+    element on sampled row blocks, at one layer (stage capture runs the batch
+    on one stream, so every launch covers all rows). 64 images are 243 whole
+    192-row tiles; 24 images (17,496 rows) end in a partial one of 24 rows,
+    whose rows past the last are read but never stored."""
     dims = S.SO400M.with_depth(1)
-    _flush(f"B=64 layer-0 stages on sampled rows, fp8={fp8}")
-    model, wt = make_model(V, dims, 2, max_batch=64, fp8=fp8)
+    _flush(f"B={batch} layer-0 stages on sampled rows, fp8={fp8}")
+    model, wt = make_model(V, dims, 2, max_batch=batch, fp8=fp8)
     model.debug_capture(0)
-    x = S.make_pixels(dims, 64, 2)
+    x = S.make_pixels(dims, batch, 2)
     y = run(model, x)
     assert np.isfinite(y).all()
-    check_stages_rows(model, wt, x, dims, fp8, 64, _band_rows(64 * dims.tokens))
+    check_stages_rows(model, wt, x, dims, fp8, batch, _band_rows(batch * dims.tokens))
     model.close()
 
 
