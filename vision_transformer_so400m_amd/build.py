@@ -32,8 +32,9 @@ FLAGS = [
 ]
 
 
-# Per-file additions. attention.hip: scores are never NaN (padded keys are -inf),
-# so max needs no NaN canonicalisation of its operands.
+# Per-file additions. attention.hip (the encoder's attention kernels only; the
+# MAP probe attention lives in map.hip): scores are never NaN (padded keys are
+# -inf), so max needs no NaN canonicalisation of its operands.
 FILE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
 
 

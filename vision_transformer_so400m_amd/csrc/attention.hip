@@ -32,11 +32,6 @@
 // Padding work that is skipped: a wave whose queries all lie past T only
 // helps move K and V into LDS, and a last key block whose second 32-key half
 // lies past T leaves that half out (its probabilities would be exact zeros).
-//
-// map_attn: MAP-head probe attention, one query per (image, head) against the
-// T encoder tokens (page "Single-layer SigLIP vision benchmark", intro: one
-// shared learned probe, its own query projection, one fused KV projection).
-// Memory-bound: it reads K and V once (2 x T x 72 x 2 bytes per head).
 #include "common.h"
 
 #include <type_traits>
@@ -1293,89 +1288,6 @@ hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, 
   }
 }
 
-constexpr int kMapMaxT = 4096;
-
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-template <bool OUT_FP8>
-__global__ __launch_bounds__(256) void map_attn_kernel(
-    const f16* __restrict__ q, const f16* __restrict__ kv, int64_t ldkv, int64_t voff,
-    void* __restrict__ o, int64_t ldo, int T, int D, float sl2, float out_scale) {
-  __shared__ float sq[80];
-  __shared__ float sp[kMapMaxT];
-  __shared__ float red[4];
-  __shared__ float part[32][80];
-
-  const int t = threadIdx.x;
-  const int hc = blockIdx.x * D;
-  const int b = blockIdx.y;
-  const f16* base = kv + (int64_t)b * T * ldkv + hc;
-  if (t < D) sq[t] = (float)q[hc + t] * sl2;
-  __syncthreads();
-
-  const int nch = D >> 3;
-  float lmax = kNegInf;
-  for (int key = t; key < T; key += 256) {
-    const f16* kr = base + (int64_t)key * ldkv;
-    float s = 0.0f;
-    for (int ch = 0; ch < nch; ++ch) {
-      const f16x8 x = *reinterpret_cast<const f16x8*>(kr + 8 * ch);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += (float)x[i] * sq[8 * ch + i];
-    }
-    sp[key] = s;
-    lmax = fmaxf(lmax, s);
-  }
-  const float M = block_max(lmax, red);
-  float lsum = 0.0f;
-  for (int key = t; key < T; key += 256) {
-    const float p = __builtin_amdgcn_exp2f(sp[key] - M);
-    sp[key] = p;
-    lsum += p;
-  }
-  const float L = block_sum(lsum, red);  // includes a barrier: sp[] complete
-
-  const int ng = min(256 / nch, 32);
-  const int grp = t / nch, ch = t % nch;
-  if (grp < ng) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int key = grp; key < T; key += ng) {
-      const f16x8 x = *reinterpret_cast<const f16x8*>(base + (int64_t)key * ldkv + voff + 8 * ch);
-      const float p = sp[key];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += p * (float)x[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part[grp][8 * ch + i] = acc[i];
-  }
-  __syncthreads();
-  if (t < D) {
-    float s = 0.0f;
-    for (int g = 0; g < ng; ++g) s += part[g][t];
-    const float r = s / L;
-    if constexpr (OUT_FP8) {
-      reinterpret_cast<uint8_t*>(o)[(int64_t)b * ldo + hc + t] =
-          (uint8_t)(cvt_pk_e4m3(r * out_scale, 0.0f, 0u, false) & 0xFF);
-    } else {
-      reinterpret_cast<f16*>(o)[(int64_t)b * ldo + hc + t] = (f16)r;
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_flash_attention(const f16* q, const f16* k, const f16* v, int64_t ld, void* o,
@@ -1486,21 +1398,6 @@ hipError_t launch_flash_attention_vt8(const void* q, const void* k, int64_t ld, 
     case 161: return launch_vt8_d<80, true>(q, k, ld, vt, vt_ld, o, ldo, batch, heads, tokens, sl2, out_fp8, out_scale, v_scale, s);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_map_attention(const f16* q, const f16* kv, int64_t ldkv, int64_t v_offset, void* o,
-                                int64_t ldo, int batch, int heads, int tokens, int head_dim,
-                                float scale, bool out_fp8, float out_scale, hipStream_t s) {
-  if (batch < 1 || heads < 1 || tokens < 1 || tokens > kMapMaxT || head_dim < 8 || head_dim > 80 ||
-      (head_dim & 7) || (ldkv & 7) || (v_offset & 7) || batch > 65535)
-    return hipErrorInvalidValue;
-  const float sl2 = scale * 1.4426950408889634f;
-  dim3 grid(heads, batch);
-  if (out_fp8)
-    hipLaunchKernelGGL(map_attn_kernel<true>, grid, dim3(256), 0, s, q, kv, ldkv, v_offset, o, ldo, tokens, head_dim, sl2, out_scale);
-  else
-    hipLaunchKernelGGL(map_attn_kernel<false>, grid, dim3(256), 0, s, q, kv, ldkv, v_offset, o, ldo, tokens, head_dim, sl2, out_scale);
-  return hipGetLastError();
 }
 
 }  // namespace siglip
