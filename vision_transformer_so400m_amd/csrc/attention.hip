@@ -36,7 +36,6 @@
 
 #include <type_traits>
 
-
 namespace siglip {
 namespace {
 
@@ -426,7 +425,6 @@ __global__ __launch_bounds__(256, MIN_WG) void flash_attn_vt_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   // constant V^T rows of every stage: row D = 1 (the PV product then also
   // yields each query's sum of the F16 probabilities it used), rows D+1..95 = 0
-  // (row-major V brings its padding with every transfer)
   constexpr int ZCH = (VROWS - D) * VV_PITCH / 16;
   for (int i = t; i < VT_STAGES * ZCH; i += 256) {
     const int r = i % ZCH;
