@@ -1058,12 +1058,13 @@ int static_scratch(void** out) {
 
 // Standalone attention. Head widths the streaming kernel takes (64, 72, 80)
 // run the encoder's own kernel: V is first transposed per image into V^T
-// rows (zeros past the last token), in `scratch` when the caller supplies
-// one of scratch_bytes, else in the library's staging buffer. Other head
-// widths run the register-staged kernel, which needs no staging.
+// rows (zeros past the last token), in stage_buf (a device address of
+// stage_bytes) when the caller supplies one, else in the library's staging
+// buffer. Other head widths run the register-staged kernel, which needs no
+// staging.
 int attention_impl(const void* q, const void* k, const void* v, int64_t ld, void* o, int32_t batch, int32_t heads,
-                   int32_t tokens, int32_t head_dim, float scale, void* hip_stream, void* scratch,
-                   size_t scratch_bytes) {
+                   int32_t tokens, int32_t head_dim, float scale, void* hip_stream, void* stage_buf,
+                   size_t stage_bytes) {
   if (!q || !k || !v || !o) return fail(SIGLIP_E_INVALID_ARG, "null q, k, v or o");
   if (batch < 1 || heads < 1 || tokens < 1 || batch > 65535 || heads > 65535)
     return fail(SIGLIP_E_INVALID_ARG, "batch, heads and tokens must be >= 1 (batch, heads <= 65535)");
@@ -1081,13 +1082,13 @@ int attention_impl(const void* q, const void* k, const void* v, int64_t ld, void
   if (flash_attention_vt_supported(head_dim)) {
     const int64_t vt_ld = round_up(tokens, 64);
     const size_t need = (size_t)batch * (size_t)width * (size_t)vt_ld * 2;
-    void* vt = scratch;
+    void* vt = stage_buf;
     if (!vt) {
       const int st = vt_staging(need, &vt);
       if (st != SIGLIP_OK) return st;
-    } else if (need > scratch_bytes) {
-      return fail(SIGLIP_E_INVALID_ARG, "V^T staging needs " + std::to_string(need) + " bytes, scratch holds " +
-                                            std::to_string(scratch_bytes));
+    } else if (need > stage_bytes) {
+      return fail(SIGLIP_E_INVALID_ARG, "V^T staging needs " + std::to_string(need) + " bytes, the buffer holds " +
+                                            std::to_string(stage_bytes));
     }
     e = launch_vt_transpose(static_cast<const f16*>(v), ld, batch, tokens, (int)width, static_cast<f16*>(vt), vt_ld,
                             s);
