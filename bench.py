@@ -70,6 +70,36 @@ def kernel_flops(cls, d, batch):
     }.get(cls)
 
 
+def class_rooflines(per_class, calls, d, batch, fp8):
+    """Each encoder kernel class against its own roofline, from the mean
+    HIP-event time per launch of the breakdown pass: the GEMMs against the
+    dense MFMA peak of their operand type, attention against the dense F16
+    peak, LayerNorm against HBM bandwidth (per launch: 2,304 bytes read per
+    row, 1,152 written as e4m3 codes or 2,304 as F16; the 54 encoder
+    LayerNorms of an e4m3 call write codes, the final one F16, the MAP head's
+    one has `batch` rows)."""
+    M, W = batch * d.tokens, d.width
+    out = {}
+    for k, (ms, n) in per_class.items():
+        if not n:
+            continue
+        s_per_launch = ms / n / 1e3
+        if k in ("EMBED", "QKV", "OUT_PROJ", "MLP_UP", "MLP_DOWN", "ATTENTION"):
+            peak = PEAK["f16_mfma_tflops"] if (k == "ATTENTION" or not fp8) else PEAK["fp8_mfma_tflops"]
+            a = kernel_flops(k, d, batch) / s_per_launch / 1e12
+            out[k] = {"bound": "mfma", "achieved": round(a, 1), "peak": peak, "unit": "TFLOP/s",
+                      "frac": round(a / peak, 4)}
+        elif k == "LAYERNORM":
+            enc = 2 * d.depth
+            out_b = W if fp8 else 2 * W
+            total = enc * M * (2 * W + out_b) + M * 4 * W + batch * (2 * W + out_b)
+            per_launch = total / (enc + 2)
+            a = per_launch / s_per_launch / 1e9
+            out[k] = {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK["hbm_gbs"], "unit": "GB/s",
+                      "frac": round(a / PEAK["hbm_gbs"], 4), "bytes_per_launch": round(per_launch)}
+    return out
+
+
 _COMMENT = re.compile(r'("(?:\\.|[^"\\])*")|//[^\n]*|/\*.*?\*/', re.S)
 
 
@@ -380,6 +410,7 @@ def main():
     kernels = {k: {"avg_us": round(ms * 1e3 / n, 2), "launches_per_step": n // prof_steps,
                    "share": round(ms / max(1e-9, sum(v[0] for v in per_class.values())), 4)}
                for k, (ms, n) in per_class.items() if n}
+    roofline_by_class = class_rooflines(per_class, prof_steps, d, B, cfg["fp8"])
     # the dominant kernel: the class with the largest summed launch time
     dom = max(per_class, key=lambda k: per_class[k][0] if kernel_flops(k, d, B) else -1)
 
@@ -469,6 +500,7 @@ def main():
         "f16_1layer_latency": c01,
         "attention_b32_t729": c2,
         "kernels": kernels,
+        "roofline_by_class": roofline_by_class,
         "roofline": roofline,
         "context": {"ipu_27layer_b1_images_per_s": 110.4, "ipu_27layer_b2_images_per_s": 126.1,
                     "note": "Graphcore IPU figures from the pages (FP8 projections), another machine"},
