@@ -975,8 +975,16 @@ __global__ __launch_bounds__(256, 3) void flash_attn_vt8_kernel(
 // written once. VROW: vt is V row-major (rows of stride ld, head h at column
 // h * D, as q and k), read through the transposing LDS reads; vt_ld is not
 // used.
-template <int D, bool OUT_FP8, bool VROW = false>
-__global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
+//
+// NS > 1 (key split, as in split-KV decoding): the workgroup holds NS groups
+// of the four query waves, group s taking key blocks [s nkb / NS, (s + 1)
+// nkb / NS) through a K/V ring of its own, so a grid of one round runs NS
+// waves per SIMD instead of one. Groups 1 .. NS-1 then leave their O^T
+// partial sums (with the probability-sum row) and references in LDS, and
+// group 0 rescales each to the largest reference and adds them in group
+// order: the same bits for every batch, not those of NS = 1.
+template <int D, bool OUT_FP8, bool VROW = false, int NS = 1>
+__global__ __launch_bounds__(256 * NS, NS == 1 ? 2 : 1) void flash_attn_vt16_kernel(
     const f16* __restrict__ q, const f16* __restrict__ k, int64_t ld, const f16* __restrict__ vt,
     int64_t vt_ld, void* __restrict__ o, int64_t ldo, int T, int H, int nqb, float c, float out_scale) {
   static_assert(D % 8 == 0 && D >= 64 && D <= 80, "head width");
@@ -996,12 +1004,14 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
   constexpr int PER_WAVE = (NDMA + NW - 1) / NW;
   constexpr float kTau = 8.0f;                     // rescale only when a row max grows by > 2^8
   constexpr int STAGES = 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE + 1024];
-  uint8_t* trash = smem + STAGES * STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGES * STAGE + 1024];
+  uint8_t* trash = smem + NS * STAGES * STAGE;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane((t >> 6) % NW);  // query wave
+  const int sp = __builtin_amdgcn_readfirstlane((t >> 6) / NW);    // key split: its own ring
+  uint8_t* const ring = smem + sp * STAGES * STAGE;
   const int fq = lane & 15;  // query of the wave (MFMA column)
   const int g = lane >> 4;   // lane group
   const int L = xcd_block(blockIdx.x, gridDim.x);
@@ -1025,9 +1035,9 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
       qf[ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   __builtin_amdgcn_s_waitcnt(0);  // as in flash_attn_vt_kernel: Q complete before the block loop
-  if constexpr (VROW) vrow_pad<NDC>(smem, STAGES, STAGE, KBYTES, t, NW * 64);
+  if constexpr (VROW) vrow_pad<NDC>(smem, NS * STAGES, STAGE, KBYTES, t, NS * NW * 64);
   constexpr int ZCH = VROW ? 0 : (VR - D) * VV_PITCH / 16;
-  for (int i = t; i < STAGES * ZCH; i += NW * 64) {
+  for (int i = t; i < NS * STAGES * ZCH; i += NS * NW * 64) {
     const int r = i % ZCH;
     uint8_t* z = smem + (i / ZCH) * STAGE + KBYTES + D * VV_PITCH + r * 16;
     const int one = 0x3C003C00;  // two F16 ones
@@ -1073,7 +1083,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
   }
   auto issue = [&](int kb) {
     const int key0 = kb * KB;
-    uint8_t* st = smem + (kb % STAGES) * STAGE;
+    uint8_t* st = ring + (kb % STAGES) * STAGE;
     const bool tail = key0 + KB > T;  // keys past T re-read token T-1
     if (!tail) {
       // every slot lands at its KiB of the stage (the V part starts at NK
@@ -1198,6 +1208,10 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
   // after the loop, so the loop holds one form of the block
   const bool active = qb * QWG + wave * 16 < T;
   const int nkb = (T + KB - 1) / KB;
+  // key split sp: blocks kb0 .. kb0 + ns - 1; the last split has the most
+  // (nmax) and the masked last block. Every split steps through nmax rounds
+  // so that all waves meet the same barriers.
+  const int kb0 = sp * nkb / NS, ns = (sp + 1) * nkb / NS - kb0, nmax = (nkb + NS - 1) / NS;
   using full = std::integral_constant<int, 2>;
   using half = std::integral_constant<int, 1>;
   using yes = std::true_type;
@@ -1206,26 +1220,63 @@ __global__ __launch_bounds__(256, 2) void flash_attn_vt16_kernel(
   // has real lanes), so at most (STAGES - 2) blocks' worth may stay in flight
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
-    if (p < nkb) issue(p);
-  for (int kb = 0; kb < nkb - 1; ++kb) {
-    if (kb + STAGES - 2 < nkb)
+    if (p < ns) issue(kb0 + p);
+  for (int i = 0; i < nmax - 1; ++i) {
+    const int kb = kb0 + i;
+    if (i + STAGES - 2 < ns)
       attn_wait_vmcnt<(STAGES - 2) * PER_WAVE>();
     else
       attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // block kb in LDS; block kb-1's stage free
-    if (kb + STAGES - 1 < nkb) issue(kb + STAGES - 1);
-    if (active) block(smem + (kb % STAGES) * STAGE, kb * KB, full(), no());
+    if (i + STAGES - 1 < ns) issue(kb + STAGES - 1);
+    if (active && i < ns) block(ring + (kb % STAGES) * STAGE, kb * KB, full(), no());
   }
   {
-    const int kb = nkb - 1, key0 = kb * KB;
+    // round nmax - 1: the last block of the splits that have nmax blocks
+    // (masking is a no-op but for the last split's)
+    const int kb = kb0 + nmax - 1, key0 = kb * KB;
     attn_wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    const uint8_t* st = smem + (kb % STAGES) * STAGE;
-    if (active) {
+    const uint8_t* st = ring + (kb % STAGES) * STAGE;
+    if (active && nmax == ns) {
       if (key0 + 32 >= T)
         block(st, key0, half(), yes());
       else
         block(st, key0, full(), yes());
+    }
+  }
+  if constexpr (NS > 1) {
+    // splits 1 .. NS-1 leave their O^T partial sums (the probability-sum row
+    // included) and references in LDS; split 0 rescales every split to the
+    // largest reference and adds them in split order
+    constexpr int PB = NT * 1024 + 256;  // bytes per (split, query wave)
+    static_assert((NS - 1) * NW * PB <= NS * STAGES * STAGE, "partials fit in the rings");
+    __syncthreads();  // every wave is done with the rings
+    if (sp > 0 && active) {
+      uint8_t* pp = smem + ((sp - 1) * NW + wave) * PB;
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) *reinterpret_cast<f32x4*>(pp + dt * 1024 + 16 * lane) = oacc[dt];
+      *reinterpret_cast<float*>(pp + NT * 1024 + 4 * lane) = m_run;
+    }
+    __syncthreads();
+    if (sp > 0 || !active) return;
+    float mref = m_run;  // query fq's largest reference over the splits
+#pragma unroll
+    for (int s2 = 1; s2 < NS; ++s2)
+      mref = fmaxf(mref, *reinterpret_cast<const float*>(smem + ((s2 - 1) * NW + wave) * PB + NT * 1024 + 4 * lane));
+    const float a0 = __builtin_amdgcn_exp2f((m_run - mref) * c);
+#pragma unroll
+    for (int dt = 0; dt < NT; ++dt) oacc[dt] *= a0;
+#pragma unroll
+    for (int s2 = 1; s2 < NS; ++s2) {
+      const uint8_t* pp = smem + ((s2 - 1) * NW + wave) * PB;
+      const float a = __builtin_amdgcn_exp2f((*reinterpret_cast<const float*>(pp + NT * 1024 + 4 * lane) - mref) * c);
+#pragma unroll
+      for (int dt = 0; dt < NT; ++dt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(pp + dt * 1024 + 16 * lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[dt][r] = fmaf(a, v[r], oacc[dt][r]);
+      }
     }
   }
   // the probability sum sits in O^T row D: tile D / 16, lane group (D % 16) / 4, register D % 4
@@ -1257,13 +1308,31 @@ hipError_t launch_vt_d(const void* q, const void* k, int64_t ld, const f16* vt, 
   // 16-query kernel, the same bits (729 tokens, 16 heads, head dim 72, batch
   // 1 / 2: 20.2 -> 19.3 us, 21.5 -> 20.4 us with eight waves per workgroup;
   // four waves, one per SIMD, 18.9 -> 16.4 us at batch 1; deeper K/V rings
-  // did not help; from batch 3 on the 32-query kernel is as fast or faster)
+  // did not help; from batch 3 on the 32-query kernel is as fast or faster).
+  // With row-major V, three key splits per workgroup: 16.5 -> 14.0 us at
+  // batch 1 (splits over workgroups, combined by the last to arrive, took
+  // 81 us: each agent-scope release and acquire writes back and invalidates
+  // an XCD's L2)
   if constexpr (!QK8) {
     if (blocks <= 256) {
       const int nq16 = (tokens + 63) / 64;
       const unsigned nb = (unsigned)(nq16 * heads * batch);
       const f16* q16 = static_cast<const f16*>(q);
       const f16* k16 = static_cast<const f16*>(k);
+      if constexpr (VROW) {
+        // row-major V (the encoder's one-round calls): three key splits per
+        // workgroup when one image's grid is at most one workgroup per CU,
+        // whatever the batch, so every batch adds the same partials
+        if (nq16 * heads <= 256) {
+          if (out_fp8)
+            hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true, true, 3>), dim3(nb), dim3(768), 0, s, q16, k16, ld,
+                               vt, vt_ld, o, ldo, tokens, heads, nq16, sl2, out_scale);
+          else
+            hipLaunchKernelGGL((flash_attn_vt16_kernel<D, false, true, 3>), dim3(nb), dim3(768), 0, s, q16, k16, ld,
+                               vt, vt_ld, o, ldo, tokens, heads, nq16, sl2, out_scale);
+          return hipGetLastError();
+        }
+      }
       if (out_fp8)
         hipLaunchKernelGGL((flash_attn_vt16_kernel<D, true, VROW>), dim3(nb), dim3(256), 0, s, q16, k16, ld, vt, vt_ld,
                            o, ldo, tokens, heads, nq16, sl2, out_scale);

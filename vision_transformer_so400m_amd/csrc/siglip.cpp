@@ -535,7 +535,7 @@ class LaunchTimer {
   size_t pair_ = 0;
 };
 
-void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, hipStream_t s) {
+void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, hipStream_t s, bool vrow) {
   const int M = B * m->tokens;
   const int W = m->width;
   const int e = m->esz();
@@ -557,7 +557,6 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
     LaunchTimer lt(m, SIGLIP_K_EMBED, s);
     gemm(m, m->embed, A.xp, m->patch_pad, M, A.h, W, EPI_BIAS_POS, false, nullptr, 0, s);
   }
-  const bool vrow = vrow_call(m, B);  // V row-major in the QKV rows, no V^T
   if (m->vt_path && !vrow && m->tokens_pad > m->tokens) {
     // V^T columns past the last token are read by the last key block: zeros
     LaunchTimer lt(m, SIGLIP_K_INPUT, s);
@@ -731,16 +730,20 @@ void encode_part(siglip_model* m, const Acts& A, const f16* x, int B, f16* out, 
 // tiles, an attention or LayerNorm phase next to a GEMM).
 void encode_impl(siglip_model* m, const f16* x, int B, f16* out, hipStream_t s) {
   const bool split = B >= 2 && m->side && m->capture_layer < 0 && m->timing_mask == 0;
+  // V row-major in the QKV rows (no V^T) and the key-split attention: chosen
+  // for the whole call, so both halves run the attention form of the
+  // one-stream run
+  const bool vrow = vrow_call(m, B);
   if (!split) {
-    encode_part(m, acts_at(m, 0), x, B, out, s);
+    encode_part(m, acts_at(m, 0), x, B, out, s, vrow);
     return;
   }
   const int B0 = (B + 1) / 2;
   hip_check(hipEventRecord(m->fork_ev, s), "fork record");
   hip_check(hipStreamWaitEvent(m->side, m->fork_ev, 0), "fork wait");
-  encode_part(m, acts_at(m, 0), x, B0, out, s);
+  encode_part(m, acts_at(m, 0), x, B0, out, s, vrow);
   encode_part(m, acts_at(m, B0), x + (int64_t)B0 * m->tokens * m->patch_dim, B - B0, out + (int64_t)B0 * m->width,
-              m->side);
+              m->side, vrow);
   hip_check(hipEventRecord(m->join_ev, m->side), "join record");
   hip_check(hipStreamWaitEvent(s, m->join_ev, 0), "join wait");
 }
