@@ -692,12 +692,14 @@ def test_head_dims_64_and_80_stages_and_end_to_end(V, hd, mode):
 
 
 @pytest.mark.parametrize("fp8", [False, True], ids=["f16", "fp8"])
-@pytest.mark.parametrize("tokens", [1, 65, 1025])
+@pytest.mark.parametrize("tokens", [1, 65, 777, 1025])
 def test_token_counts_degenerate_and_ragged(V, tokens, fp8):
     """Other token counts through the whole path at batch 2 (two streams):
     one token (every softmax has a single key and the MAP probe a single
     token), 65 (one key past a 64-key block, one row past a 64-row GEMM
-    tile), 1025 (one key past sixteen blocks, one query past eight
+    tile; the key-split attention's first split gets no block), 777 (13
+    key blocks split 4/4/5 over the three wave groups, the last block 9
+    keys), 1025 (one key past sixteen blocks, one query past eight
     128-query workgroups, and above the 1024 tokens of the folded MAP head,
     so the explicit K/V projection runs). Stage by stage and end to end."""
     dims = S.ModelDims(tokens=tokens, depth=1)
